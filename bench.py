@@ -1,0 +1,273 @@
+#!/usr/bin/env python3
+"""Benchmark of calibrated block-sparse attention on one MI355X.
+
+A step is one block-sparse attention forward (calibatt_sparse_attn_fwd) over
+a Wan 2.1 14B-shaped 720p self-attention layer: 40 heads, N = 75600 tokens
+(21 frames x 45 x 80), D = 128, bf16, per-head seeded block masks at 62.5%
+block sparsity (frame band + random blocks, diagonal kept). Inputs are
+resident in HBM before timing starts.
+
+Prints one JSON line. `value` is the effective TFLOP/s over kept blocks:
+4 * 128 * 128 * 128 FLOP per kept (query block, key block) pair divided by
+the measured time. Also reported: the speedup against the same kernel run
+with every block kept, the roofline of the kernel (bf16 MFMA peak), the
+other layer shapes and the calibration pass, and the fp64 CPU oracle timed
+on a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-extras] [--no-cpu]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2516.6     # 256 CU x 4 SIMD x 1024 FLOP/clk x 2.4 GHz (AMD spec: 2.5 PFLOP/s)
+HBM_PEAK_GBS = 8000.0
+PAIR_FLOP = 4.0 * 128 * 128 * 128  # QK^T and PV of one 128x128 block, D = 128
+METRIC = "effective TFLOP/s on kept blocks + speedup vs dense mask, Wan-720p shape, 1 GPU"
+KERNEL_SOURCES = ("calibrated_block_sparse_amd/csrc/attn_fwd.hip",
+                  "calibrated_block_sparse_amd/csrc/device_common.h")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def time_launches(fn, steps: int, warmup: int):
+    """Per-launch durations (ms) from events on torch's current stream (the
+    stream the library launches on), plus the bracketed wall time of all
+    steps."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    outer0, outer1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    outer0.record()
+    for i in range(steps):
+        starts[i].record()
+        fn()
+        ends[i].record()
+    outer1.record()
+    torch.cuda.synchronize()
+    per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    return per, outer0.elapsed_time(outer1)
+
+
+def attn_case(cbs, name: str, steps: int, warmup: int, dense: bool = False):
+    from synth import ATTN_WORKLOADS, block_mask, qkv, repeat_flags
+    w = ATTN_WORKLOADS[name]
+    q, k, v = qkv(w, device="cuda")
+    o = torch.empty_like(q)
+    mask = np.ones((w.heads, w.n_blocks, w.n_blocks), np.uint8) if dense else block_mask(w)
+    off, idx = cbs.compile_skiplist(torch.from_numpy(mask).cuda())
+    flags = repeat_flags(w)
+    grid = None
+    if flags.any():
+        grid = (w.grid.frames, w.grid.rows, w.grid.cols, w.anchors)
+    else:
+        flags = None
+    pairs = int(idx.numel()) if flags is None else int(
+        mask[flags == 0].sum() + int(flags.sum()) * -(-(w.grid.frames * w.anchors * w.grid.cols) // 128) * w.n_blocks)
+
+    def step():
+        cbs.calibatt_sparse_attn_fwd(q, k, v, o, off, idx, w.scale, flags, grid)
+
+    per, total = time_launches(step, steps, warmup)
+    return dict(workload=w, pairs=pairs, per_ms=per, total_ms=total, mask=mask, tensors=(q, k, v))
+
+
+def calibration_case(cbs, draws: int):
+    """Calibration shape: energies of `draws` prompt draws, greedy selection
+    at eps(t) for the three steps, vote accumulation, then binarisation and
+    kept-list compilation. Returns per-stage times in ms."""
+    from synth import CALIB_WORKLOADS, calib_basis, calib_draw, n_blocks
+    w = CALIB_WORKLOADS["calibration_480p"]
+    R = n_blocks(w.n_tokens)
+    basis = calib_basis(w, "cuda")
+    energy = torch.empty(w.heads, R, R, dtype=torch.float32, device="cuda")
+    ws = torch.empty(cbs.calibatt_block_energy_workspace(w.heads, w.n_tokens), dtype=torch.uint8,
+                     device="cuda")
+    votes = {t: torch.zeros(w.heads, R, R, dtype=torch.uint8, device="cuda") for t in w.steps}
+    efx = {t: cbs.calibatt_eps_fx(t, w.total_steps, w.eps_floor, w.eps_start, w.eps_rate)
+           for t in w.steps}
+    t_energy = t_select = 0.0
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    for p in range(draws):
+        q, k = calib_draw(w, p, basis, "cuda")
+        torch.cuda.synchronize()
+        ev[0].record()
+        cbs.calibatt_block_energy(q, k, energy, w.scale, ws)
+        ev[1].record()
+        for t in w.steps:
+            cbs.calibatt_build_mask(energy, efx[t], votes[t])
+        ev[2].record()
+        torch.cuda.synchronize()
+        t_energy += ev[0].elapsed_time(ev[1])
+        t_select += ev[1].elapsed_time(ev[2])
+    mask = torch.empty(w.heads, R, R, dtype=torch.uint8, device="cuda")
+    off = torch.empty(w.heads * R + 1, dtype=torch.int32, device="cuda")
+    idx = torch.empty(w.heads * R * R, dtype=torch.int32, device="cuda")
+    t0 = time.perf_counter()
+    kept = {}
+    for t in w.steps:
+        nnz = cbs.calibatt_finalize_mask(votes[t], draws, *w.rho, mask, off, idx)
+        kept[t] = nnz / (w.heads * R * R)
+    t_fin = (time.perf_counter() - t0) * 1e3
+    flop_energy = 2 * 2.0 * w.heads * (R * 128) ** 2 * w.head_dim   # two QK^T passes
+    return {
+        "workload": "calibration_480p", "heads": w.heads, "n_tokens": w.n_tokens, "draws": draws,
+        "energy_ms_per_draw": round(t_energy / draws, 3),
+        "energy_tflops": round(flop_energy / (t_energy / draws * 1e-3) / 1e12, 1),
+        "select_votes_ms_per_draw_3eps": round(t_select / draws, 3),
+        "finalize_ms_3steps_incl_sync": round(t_fin, 3),
+        "kept_fraction_by_step": {str(t): round(v, 4) for t, v in kept.items()},
+    }
+
+
+def cpu_baseline(case, seconds: float = 15.0):
+    """The fp64 oracle on host cores over whole query blocks of head 0 of the
+    same workload, until about `seconds` of work; scaled to TFLOP/s over the
+    kept pairs it covered."""
+    import oracle
+    from synth import bf16_bits
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    w = case["workload"]
+    mask = case["mask"]
+    q, k, v = case["tensors"]
+    qb, kb, vb = (oracle.as_f64(bf16_bits(t[0])) for t in (q, k, v))
+    pairs = 0
+    blocks = 0
+    t0 = time.perf_counter()
+    r = 0
+    while time.perf_counter() - t0 < seconds and r < w.n_blocks:
+        cols = np.flatnonzero(mask[0, r])
+        oracle.block_sparse_attention_block(qb, kb, vb, w.scale, cols, r)
+        pairs += cols.size
+        blocks += 1
+        r += 1
+    dt = time.perf_counter() - t0
+    return {"value": round(pairs * PAIR_FLOP / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{w.name} head 0, query blocks 0..{blocks - 1} ({pairs} kept pairs, fp64 numpy), {dt:.1f} s"}
+
+
+def traffic_record():
+    """HBM bytes per launch from committed rocprofv3 counter runs, valid only
+    while the kernel sources are unchanged."""
+    p = os.path.join(ROOT, "profiles", "attn_fwd_wan21_720p_counters.json")
+    if not os.path.exists(p):
+        return None
+    rec = json.load(open(p))
+    if rec.get("kernel_hash") != kernel_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="wan21_720p_layer")
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calib-draws", type=int, default=4)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(heads shard across GPUs without communication; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    import calibrated_block_sparse_amd as cbs
+    cbs.load_library()
+
+    log(f"[bench] {args.workload}: sparse mask, {args.steps} steps after {args.warmup} warmup")
+    sp = attn_case(cbs, args.workload, args.steps, args.warmup)
+    w = sp["workload"]
+    ms = float(np.median(sp["per_ms"]))
+    ms_step = sp["total_ms"] / args.steps
+    flop = sp["pairs"] * PAIR_FLOP
+    eff = flop / (ms_step * 1e-3) / 1e12
+    log(f"[bench] sparse: {ms_step:.3f} ms/step, {eff:.1f} TFLOP/s effective")
+
+    log("[bench] dense mask (every block kept)")
+    dn = attn_case(cbs, args.workload, max(3, args.steps // 4), 2, dense=True)
+    dense_ms = float(np.median(dn["per_ms"]))
+    dense_tflops = dn["pairs"] * PAIR_FLOP / (dense_ms * 1e-3) / 1e12
+    del dn
+
+    per_launch_ms = float(np.mean(sp["per_ms"]))
+    achieved = flop / (per_launch_ms * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(eff, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "heads": w.heads, "n_tokens": w.n_tokens,
+                   "head_dim": w.head_dim, "block": 128, "block_sparsity": w.sparsity,
+                   "kept_pairs": sp["pairs"], "frames_x_rows_x_cols": [w.grid.frames, w.grid.rows, w.grid.cols]},
+        "speedup_vs_dense_mask": round(dense_ms / ms, 3),
+        "dense_mask": {"ms": round(dense_ms, 3), "tflops": round(dense_tflops, 1)},
+        "sparse_ms_p10_p50_p90": [round(float(x), 4) for x in np.percentile(sp["per_ms"], [10, 50, 90])],
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": traffic_record(), "kernel": "calibatt::attn_fwd_kernel",
+                     "kernel_hash": kernel_hash()},
+    }
+    if not args.no_extras:
+        extras = {}
+        for name in ("wan21_480p_layer", "mochi1_480p_layer"):
+            if name == args.workload:
+                continue
+            log(f"[bench] extra: {name}")
+            c = attn_case(cbs, name, 10, 3)
+            m = float(np.median(c["per_ms"]))
+            extras[name] = {"ms": round(m, 3), "pairs": c["pairs"],
+                            "effective_tflops": round(c["pairs"] * PAIR_FLOP / (m * 1e-3) / 1e12, 1)}
+            del c
+        log(f"[bench] extra: calibration, {args.calib_draws} draws")
+        extras["calibration"] = calibration_case(cbs, args.calib_draws)
+        out["extras"] = extras
+    if not args.no_cpu:
+        log("[bench] cpu baseline (fp64 oracle)")
+        out["cpu_baseline"] = cpu_baseline(sp)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,265 @@
+"""Python binding of libcalibatt.so (calibrated block-sparse attention for
+MI355X / gfx950).
+
+Argument marshalling only: every step runs in the library's HIP kernels.
+torch supplies device memory and the current stream. The functions keep
+the C names of include/calibatt.h; each raises CalibAttError with the
+library's message when the call fails, and load_library() raises when the
+shared library has not been built (python -m calibrated_block_sparse_amd.build).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+import torch
+
+BLOCK = 128
+HEAD_DIM = 128
+MAX_BLOCKS = 2047
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libcalibatt.so")
+
+# Every symbol include/calibatt.h declares, with its ctypes signature.
+_c = ctypes
+_p = _c.c_void_p
+SIGNATURES = {
+    "calibatt_last_error": (_c.c_char_p, []),
+    "calibatt_abi_version": (_c.c_int32, []),
+    "calibatt_sparse_attn_fwd": (_c.c_int, [_p, _p, _p, _p, _c.c_int32, _c.c_int32, _c.c_int32,
+                                            _c.c_int64, _c.c_int64, _c.c_float, _p, _p,
+                                            _c.c_int64, _p, _p, _p]),
+    "calibatt_block_energy_workspace": (_c.c_size_t, [_c.c_int32, _c.c_int32]),
+    "calibatt_block_energy": (_c.c_int, [_p, _p, _p, _c.c_int32, _c.c_int32, _c.c_int32,
+                                         _c.c_int64, _c.c_int64, _c.c_float, _p, _c.c_size_t, _p]),
+    "calibatt_eps_fx": (_c.c_uint64, [_c.c_double] * 5),
+    "calibatt_build_mask": (_c.c_int, [_p, _c.c_int32, _c.c_int32, _c.c_int32, _c.c_uint64, _p,
+                                       _p, _p]),
+    "calibatt_finalize_mask": (_c.c_int, [_p, _c.c_int32, _c.c_int32, _c.c_int32, _c.c_int32,
+                                          _c.c_int32, _p, _p, _p, _p, _p]),
+    "calibatt_compile_skiplist": (_c.c_int, [_p, _c.c_int32, _c.c_int32, _p, _p, _p, _p]),
+    "calibatt_validate_skiplist": (_c.c_int, [_p, _p, _c.c_int64, _c.c_int32, _c.c_int32]),
+}
+
+STATUS = {0: "OK", -1: "INVALID_ARG", -2: "UNSUPPORTED", -3: "BAD_SKIPLIST", -4: "WORKSPACE",
+          -5: "HIP"}
+
+
+class CalibAttError(RuntimeError):
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__(f"{fn} failed ({STATUS.get(code, code)}): {msg}")
+        self.code = code
+
+
+class Grid(ctypes.Structure):
+    """calibatt_grid: token n = f*rows*cols + y*cols + x; `anchors` rows per
+    frame are computed by repeat heads."""
+    _fields_ = [("frames", ctypes.c_int32), ("rows", ctypes.c_int32),
+                ("cols", ctypes.c_int32), ("anchors", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load_library(path: Optional[str] = None):
+    """Loads libcalibatt.so once; raises if it is missing or lacks a symbol."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} not found: build it with `python -m calibrated_block_sparse_amd.build`")
+    lib = ctypes.CDLL(p)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(fn: str, rc: int):
+    if rc != 0:
+        raise CalibAttError(fn, rc, load_library().calibatt_last_error().decode())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def n_blocks(n_tokens: int) -> int:
+    return (n_tokens + BLOCK - 1) // BLOCK
+
+
+def _attn_layout(name: str, *ts: torch.Tensor):
+    """[heads][N][128] bf16 CUDA tensors sharing one stride pattern."""
+    t0 = ts[0]
+    for t in ts:
+        if t.dtype != torch.bfloat16 or not t.is_cuda or t.dim() != 3:
+            raise ValueError(f"{name}: expected 3-d bf16 CUDA tensors [heads][N][128]")
+        if t.shape != t0.shape or t.stride() != t0.stride():
+            raise ValueError(f"{name}: q/k/v/o must share shape and strides")
+        if t.stride(2) != 1:
+            raise ValueError(f"{name}: the head dimension must be contiguous")
+    H, N, D = t0.shape
+    return H, N, D, t0.stride(0), t0.stride(1)
+
+
+def calibatt_last_error() -> str:
+    return load_library().calibatt_last_error().decode()
+
+
+def calibatt_abi_version() -> int:
+    return int(load_library().calibatt_abi_version())
+
+
+def calibatt_sparse_attn_fwd(q, k, v, o, kv_offsets, kv_indices, scale: float,
+                             repeat_flags=None, grid=None, stream=None) -> None:
+    """o <- block-sparse attention of q, k, v over the kept-block lists
+    (kv_offsets int32 [H*R+1], kv_indices int32 [nnz], CUDA tensors).
+    repeat_flags: host sequence of H ints (or None); grid: (frames, rows,
+    cols, anchors) for repeat heads."""
+    H, N, D, sh, stok = _attn_layout("calibatt_sparse_attn_fwd", q, k, v, o)
+    for t in (kv_offsets, kv_indices):
+        if t is not None and (t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("kept-block lists must be contiguous int32 CUDA tensors")
+    nnz = 0 if kv_indices is None else kv_indices.numel()
+    flags = None
+    if repeat_flags is not None:
+        arr = np.ascontiguousarray(np.asarray(repeat_flags, dtype=np.uint8))
+        if arr.shape != (H,):
+            raise ValueError("repeat_flags must have one entry per head")
+        flags = arr.ctypes.data_as(ctypes.c_void_p)
+    g = None
+    if grid is not None:
+        g = ctypes.byref(Grid(*[int(x) for x in grid]))
+    lib = load_library()
+    rc = lib.calibatt_sparse_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), H, N, D, sh, stok,
+                                      float(scale), _ptr(kv_offsets), _ptr(kv_indices), nnz,
+                                      flags, g, _stream(stream))
+    _check("calibatt_sparse_attn_fwd", rc)
+
+
+def calibatt_block_energy_workspace(heads: int, n_tokens: int) -> int:
+    return int(load_library().calibatt_block_energy_workspace(heads, n_tokens))
+
+
+def calibatt_block_energy(q, k, energy, scale: float, workspace=None, stream=None) -> None:
+    """energy (fp32 CUDA [H][R][R]) <- block energies of softmax(scale q k^T).
+    workspace: uint8 CUDA tensor of calibatt_block_energy_workspace bytes
+    (allocated here through torch when None)."""
+    H, N, D, sh, stok = _attn_layout("calibatt_block_energy", q, k)
+    R = n_blocks(N)
+    if energy.dtype != torch.float32 or not energy.is_contiguous() or energy.shape != (H, R, R):
+        raise ValueError("energy must be a contiguous fp32 tensor [H][R][R]")
+    need = calibatt_block_energy_workspace(H, N)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    rc = load_library().calibatt_block_energy(_ptr(q), _ptr(k), _ptr(energy), H, N, D, sh, stok,
+                                              float(scale), _ptr(workspace),
+                                              workspace.numel() * workspace.element_size(),
+                                              _stream(stream))
+    _check("calibatt_block_energy", rc)
+
+
+def calibatt_eps_fx(t: float, T: float, A: float, C: float, k: float) -> int:
+    return int(load_library().calibatt_eps_fx(float(t), float(T), float(A), float(C), float(k)))
+
+
+def calibatt_build_mask(energy, eps_fx: int, votes, n_sel=None, stream=None) -> None:
+    """votes (uint8 [H][R][R]) += greedy selections at eps_fx of every draw in
+    energy (fp32 [n_draws][H][R][R] or [H][R][R]); n_sel (int32
+    [n_draws][H][R]) receives the selected counts when given."""
+    e = energy if energy.dim() == 4 else energy.unsqueeze(0)
+    D_, H, R, R2 = e.shape
+    if e.dtype != torch.float32 or not e.is_contiguous() or R != R2:
+        raise ValueError("energy must be contiguous fp32 [n_draws][H][R][R]")
+    if votes.dtype != torch.uint8 or votes.shape != (H, R, R) or not votes.is_contiguous():
+        raise ValueError("votes must be contiguous uint8 [H][R][R]")
+    if n_sel is not None and (n_sel.dtype != torch.int32 or n_sel.numel() != D_ * H * R):
+        raise ValueError("n_sel must be int32 with n_draws*H*R entries")
+    rc = load_library().calibatt_build_mask(_ptr(e), D_, H, R, int(eps_fx), _ptr(votes),
+                                            _ptr(n_sel), _stream(stream))
+    _check("calibatt_build_mask", rc)
+
+
+def calibatt_finalize_mask(votes, n_prompts: int, rho_num: int, rho_den: int, mask,
+                           kv_offsets, kv_indices, stream=None) -> int:
+    """Binarise votes at rho = rho_num/rho_den into mask and compile the
+    kept-block lists; returns nnz (waits for the stream)."""
+    H, R, _ = votes.shape
+    nnz = ctypes.c_int64(0)
+    rc = load_library().calibatt_finalize_mask(_ptr(votes), H, R, int(n_prompts), int(rho_num),
+                                               int(rho_den), _ptr(mask), _ptr(kv_offsets),
+                                               _ptr(kv_indices), ctypes.byref(nnz),
+                                               _stream(stream))
+    _check("calibatt_finalize_mask", rc)
+    return int(nnz.value)
+
+
+def calibatt_compile_skiplist(mask, kv_offsets, kv_indices, stream=None) -> int:
+    """Compile a uint8 [H][R][R] block mask into kept-block lists; returns
+    nnz (waits for the stream)."""
+    H, R, R2 = mask.shape
+    if mask.dtype != torch.uint8 or R != R2 or not mask.is_contiguous():
+        raise ValueError("mask must be contiguous uint8 [H][R][R]")
+    if kv_offsets.numel() < H * R + 1 or kv_indices.numel() < H * R * R:
+        raise ValueError("kv_offsets needs H*R+1 entries and kv_indices H*R*R")
+    nnz = ctypes.c_int64(0)
+    rc = load_library().calibatt_compile_skiplist(_ptr(mask), H, R, _ptr(kv_offsets),
+                                                  _ptr(kv_indices), ctypes.byref(nnz),
+                                                  _stream(stream))
+    _check("calibatt_compile_skiplist", rc)
+    return int(nnz.value)
+
+
+def calibatt_validate_skiplist(kv_offsets, kv_indices, heads: int, n_blocks_: int) -> None:
+    """Host-side check of a kept-block list (numpy int32 arrays or CPU
+    tensors); raises CalibAttError(BAD_SKIPLIST) on the first defect."""
+    off = np.ascontiguousarray(np.asarray(kv_offsets, dtype=np.int32))
+    idx = np.ascontiguousarray(np.asarray(kv_indices, dtype=np.int32))
+    if off.size != heads * n_blocks_ + 1:
+        raise ValueError("kv_offsets must have heads*R+1 entries")
+    rc = load_library().calibatt_validate_skiplist(off.ctypes.data_as(ctypes.c_void_p),
+                                                   idx.ctypes.data_as(ctypes.c_void_p),
+                                                   idx.size, heads, n_blocks_)
+    _check("calibatt_validate_skiplist", rc)
+
+
+# ----------------------------------------------------------------------------
+# Allocating conveniences (torch allocations + the calls above)
+
+
+def compile_skiplist(mask: torch.Tensor, stream=None):
+    """(kv_offsets, kv_indices[:nnz]) on mask's device."""
+    H, R, _ = mask.shape
+    off = torch.empty(H * R + 1, dtype=torch.int32, device=mask.device)
+    idx = torch.empty(max(H * R * R, 1), dtype=torch.int32, device=mask.device)
+    nnz = calibatt_compile_skiplist(mask, off, idx, stream)
+    return off, idx[:nnz]
+
+
+def sparse_attention(q, k, v, kv_offsets, kv_indices, scale: float, repeat_flags=None,
+                     grid=None, stream=None) -> torch.Tensor:
+    o = torch.empty_like(q)
+    calibatt_sparse_attn_fwd(q, k, v, o, kv_offsets, kv_indices, scale, repeat_flags, grid, stream)
+    return o
+
+
+def block_energy(q, k, scale: float, stream=None) -> torch.Tensor:
+    H, N, _ = q.shape
+    R = n_blocks(N)
+    e = torch.empty(H, R, R, dtype=torch.float32, device=q.device)
+    calibatt_block_energy(q, k, e, scale, None, stream)
+    return e

@@ -1,0 +1,295 @@
+// C ABI of libcalibatt.so: argument validation, work decomposition and
+// launches. The declarations and their contracts are in include/calibatt.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/calibatt.h"
+#include "kernels.h"
+
+using namespace calibatt;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return CALIBATT_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(CALIBATT_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Shared checks of the bf16 [heads][N][128] tensor arguments.
+int check_tensor_layout(const char* fn, int32_t heads, int32_t n_tokens, int32_t head_dim,
+                        int64_t stride_head, int64_t stride_token) {
+  if (heads < 0 || n_tokens < 0)
+    return fail(CALIBATT_ERR_INVALID_ARG, "%s: heads (%d) and n_tokens (%d) must be >= 0", fn,
+                heads, n_tokens);
+  if (head_dim != CALIBATT_HEAD_DIM)
+    return fail(CALIBATT_ERR_UNSUPPORTED, "%s: head_dim %d unsupported (only %d)", fn, head_dim,
+                CALIBATT_HEAD_DIM);
+  if (stride_token < head_dim || stride_head < 0 || stride_token % 8 || stride_head % 8)
+    return fail(CALIBATT_ERR_INVALID_ARG,
+                "%s: strides (head %lld, token %lld) must be multiples of 8 with token >= %d", fn,
+                (long long)stride_head, (long long)stride_token, head_dim);
+  return CALIBATT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* calibatt_last_error(void) { return g_last_error.c_str(); }
+
+int32_t calibatt_abi_version(void) { return 1; }
+
+int calibatt_sparse_attn_fwd(const void* q, const void* k, const void* v, void* o, int32_t heads,
+                             int32_t n_tokens, int32_t head_dim, int64_t stride_head,
+                             int64_t stride_token, float scale, const int32_t* kv_offsets,
+                             const int32_t* kv_indices, int64_t nnz,
+                             const uint8_t* repeat_flags, const calibatt_grid* grid,
+                             void* stream) {
+  const char* fn = "calibatt_sparse_attn_fwd";
+  int rc = check_tensor_layout(fn, heads, n_tokens, head_dim, stride_head, stride_token);
+  if (rc) return rc;
+  if (heads == 0 || n_tokens == 0) return ok();
+  if (!q || !k || !v || !o) return fail(CALIBATT_ERR_INVALID_ARG, "%s: null q/k/v/o", fn);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(CALIBATT_ERR_INVALID_ARG, "%s: q/k/v/o must be 16-byte aligned", fn);
+  if (!(scale > 0.f) || !std::isfinite(scale))
+    return fail(CALIBATT_ERR_INVALID_ARG, "%s: scale must be finite and > 0", fn);
+  if (nnz < 0) return fail(CALIBATT_ERR_INVALID_ARG, "%s: nnz < 0", fn);
+
+  const int32_t R = (int32_t)ceil_div(n_tokens, CALIBATT_BLOCK);
+  std::vector<int32_t> rep_heads, sparse_heads;
+  for (int32_t h = 0; h < heads; ++h)
+    (repeat_flags && repeat_flags[h] ? rep_heads : sparse_heads).push_back(h);
+
+  AttnArgs a;
+  std::memset(&a, 0, sizeof a);
+  if (!rep_heads.empty()) {
+    if (!grid) return fail(CALIBATT_ERR_INVALID_ARG, "%s: repeat heads need a grid", fn);
+    if (grid->frames <= 0 || grid->rows <= 0 || grid->cols <= 0 ||
+        (int64_t)grid->frames * grid->rows * grid->cols != n_tokens)
+      return fail(CALIBATT_ERR_INVALID_ARG, "%s: grid %dx%dx%d does not cover N=%d", fn,
+                  grid->frames, grid->rows, grid->cols, n_tokens);
+    if (grid->anchors < 1 || grid->anchors > grid->rows)
+      return fail(CALIBATT_ERR_INVALID_ARG, "%s: anchors %d not in [1, rows=%d]", fn,
+                  grid->anchors, grid->rows);
+    a.frames = grid->frames;
+    a.rows = grid->rows;
+    a.cols = grid->cols;
+    a.anchors = grid->anchors;
+    a.anchor_queries = grid->frames * grid->anchors * grid->cols;
+  }
+  if (!sparse_heads.empty() && (!kv_offsets || (!kv_indices && nnz > 0)))
+    return fail(CALIBATT_ERR_INVALID_ARG, "%s: null kept-block list", fn);
+
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<uint16_t*>(o);
+  a.stride_head = stride_head;
+  a.stride_token = stride_token;
+  a.offsets = kv_offsets;
+  a.indices = kv_indices;
+  a.nnz = nnz;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.n_tokens = n_tokens;
+  a.n_blocks = R;
+  a.rep_tiles = (int32_t)ceil_div(a.anchor_queries, CALIBATT_BLOCK);
+
+  // Launch in chunks of at most kMaxHeadsPerLaunch heads; repeat heads (the
+  // longest tiles) come first in each launch.
+  size_t ri = 0, si = 0;
+  while (ri < rep_heads.size() || si < sparse_heads.size()) {
+    int n = 0;
+    a.n_rep = 0;
+    a.n_sparse = 0;
+    while (n < kMaxHeadsPerLaunch && ri < rep_heads.size()) { a.heads[n++] = rep_heads[ri++]; ++a.n_rep; }
+    while (n < kMaxHeadsPerLaunch && si < sparse_heads.size()) { a.heads[n++] = sparse_heads[si++]; ++a.n_sparse; }
+    const int64_t items = (int64_t)a.n_rep * a.rep_tiles + (int64_t)a.n_sparse * R;
+    if (items > 0x7fffffff) return fail(CALIBATT_ERR_UNSUPPORTED, "%s: too many tiles", fn);
+    a.n_items = (int32_t)items;
+    hipError_t e = launch_attn_fwd(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, fn);
+  }
+  return ok();
+}
+
+size_t calibatt_block_energy_workspace(int32_t heads, int32_t n_tokens) {
+  if (heads <= 0 || n_tokens <= 0) return 0;
+  return (size_t)2 * sizeof(float) * (size_t)heads * (size_t)ceil_div(n_tokens, CALIBATT_BLOCK) *
+         CALIBATT_BLOCK;
+}
+
+int calibatt_block_energy(const void* q, const void* k, float* energy, int32_t heads,
+                          int32_t n_tokens, int32_t head_dim, int64_t stride_head,
+                          int64_t stride_token, float scale, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  const char* fn = "calibatt_block_energy";
+  int rc = check_tensor_layout(fn, heads, n_tokens, head_dim, stride_head, stride_token);
+  if (rc) return rc;
+  if (heads == 0 || n_tokens == 0) return ok();
+  if (!q || !k || !energy) return fail(CALIBATT_ERR_INVALID_ARG, "%s: null q/k/energy", fn);
+  if (!aligned16(q) || !aligned16(k))
+    return fail(CALIBATT_ERR_INVALID_ARG, "%s: q/k must be 16-byte aligned", fn);
+  if (!(scale > 0.f) || !std::isfinite(scale))
+    return fail(CALIBATT_ERR_INVALID_ARG, "%s: scale must be finite and > 0", fn);
+  const int64_t R = ceil_div(n_tokens, CALIBATT_BLOCK);
+  if (R > CALIBATT_MAX_BLOCKS)
+    return fail(CALIBATT_ERR_UNSUPPORTED, "%s: %lld blocks > %d", fn, (long long)R,
+                CALIBATT_MAX_BLOCKS);
+  if ((int64_t)heads * R > 0x7fffffff) return fail(CALIBATT_ERR_UNSUPPORTED, "%s: too many tiles", fn);
+  const size_t need = calibatt_block_energy_workspace(heads, n_tokens);
+  if (!workspace || workspace_bytes < need)
+    return fail(CALIBATT_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu", fn, workspace_bytes, need);
+  if (reinterpret_cast<uintptr_t>(workspace) & 3u)
+    return fail(CALIBATT_ERR_WORKSPACE, "%s: workspace must be 4-byte aligned", fn);
+  EnergyArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.stride_head = stride_head;
+  a.stride_token = stride_token;
+  a.row_max = static_cast<float*>(workspace);
+  a.row_sum = a.row_max + (size_t)heads * R * CALIBATT_BLOCK;
+  a.energy = energy;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.n_tokens = n_tokens;
+  a.n_blocks = (int32_t)R;
+  a.heads = heads;
+  hipError_t e = launch_block_energy(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return ok();
+}
+
+uint64_t calibatt_eps_fx(double t, double T, double A, double C, double k) {
+  const double eps = A + (C - A) * std::exp(-k * t / T);
+  const double x = std::nearbyint(eps * 1099511627776.0);  // default mode: ties to even
+  if (!(x > 0.0)) return 0;
+  if (x >= 18446744073709551615.0) return ~0ull;
+  return (uint64_t)x;
+}
+
+int calibatt_build_mask(const float* energy, int32_t n_draws, int32_t heads, int32_t n_blocks,
+                        uint64_t eps_fx, uint8_t* votes, int32_t* n_sel, void* stream) {
+  const char* fn = "calibatt_build_mask";
+  if (n_draws < 0 || heads < 0 || n_blocks < 0)
+    return fail(CALIBATT_ERR_INVALID_ARG, "%s: negative size", fn);
+  if (n_draws == 0 || heads == 0 || n_blocks == 0) return ok();
+  if (n_blocks > CALIBATT_MAX_BLOCKS)
+    return fail(CALIBATT_ERR_UNSUPPORTED, "%s: %d blocks > %d", fn, n_blocks, CALIBATT_MAX_BLOCKS);
+  if (!energy || !votes) return fail(CALIBATT_ERR_INVALID_ARG, "%s: null energy/votes", fn);
+  if ((int64_t)heads * n_blocks > 0x7fffffff) return fail(CALIBATT_ERR_UNSUPPORTED, "%s: too many rows", fn);
+  hipError_t e = launch_select_votes(energy, n_draws, heads, n_blocks, eps_fx, votes, n_sel,
+                                     static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return ok();
+}
+
+static int compile_common(const char* fn, const uint8_t* src, int mode, int32_t heads,
+                          int32_t n_blocks, int32_t n_prompts, int32_t rho_num, int32_t rho_den,
+                          uint8_t* mask, int32_t* kv_offsets, int32_t* kv_indices,
+                          int64_t* nnz_out, void* stream) {
+  if (heads < 0 || n_blocks < 0) return fail(CALIBATT_ERR_INVALID_ARG, "%s: negative size", fn);
+  const int64_t rows = (int64_t)heads * n_blocks;
+  if (rows * n_blocks >= 0x7fffffffLL)
+    return fail(CALIBATT_ERR_UNSUPPORTED, "%s: heads*R*R must be < 2^31", fn);
+  if (!kv_offsets) return fail(CALIBATT_ERR_INVALID_ARG, "%s: null kv_offsets", fn);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (rows == 0) {
+    e = launch_offsets_scan(kv_offsets, 0, s);  // writes offsets[0] = 0
+    if (e != hipSuccess) return hip_fail(e, fn);
+  } else {
+    if (!src || !kv_indices || (mode == 1 && !mask))
+      return fail(CALIBATT_ERR_INVALID_ARG, "%s: null input/output", fn);
+    e = launch_row_counts(src, (int32_t)rows, n_blocks, mode, n_prompts, rho_num, rho_den, mask,
+                          kv_offsets, s);
+    if (e == hipSuccess) e = launch_offsets_scan(kv_offsets, (int32_t)rows, s);
+    if (e == hipSuccess)
+      e = launch_compact(mode == 1 ? mask : src, (int32_t)rows, n_blocks, kv_offsets, kv_indices, s);
+    if (e != hipSuccess) return hip_fail(e, fn);
+  }
+  if (nnz_out) {
+    int32_t nnz = 0;
+    e = hipMemcpyAsync(&nnz, kv_offsets + rows, sizeof nnz, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    *nnz_out = nnz;
+  }
+  return ok();
+}
+
+int calibatt_finalize_mask(const uint8_t* votes, int32_t heads, int32_t n_blocks,
+                           int32_t n_prompts, int32_t rho_num, int32_t rho_den, uint8_t* mask,
+                           int32_t* kv_offsets, int32_t* kv_indices, int64_t* nnz_out,
+                           void* stream) {
+  const char* fn = "calibatt_finalize_mask";
+  if (n_prompts < 1 || n_prompts > 255)
+    return fail(CALIBATT_ERR_INVALID_ARG, "%s: n_prompts %d not in [1, 255]", fn, n_prompts);
+  if (rho_den < 1 || rho_num < 0 || rho_num > rho_den || rho_den > (1 << 20))
+    return fail(CALIBATT_ERR_INVALID_ARG, "%s: rho %d/%d invalid", fn, rho_num, rho_den);
+  return compile_common(fn, votes, 1, heads, n_blocks, n_prompts, rho_num, rho_den, mask,
+                        kv_offsets, kv_indices, nnz_out, stream);
+}
+
+int calibatt_compile_skiplist(const uint8_t* mask, int32_t heads, int32_t n_blocks,
+                              int32_t* kv_offsets, int32_t* kv_indices, int64_t* nnz_out,
+                              void* stream) {
+  return compile_common("calibatt_compile_skiplist", mask, 0, heads, n_blocks, 0, 0, 1, nullptr,
+                        kv_offsets, kv_indices, nnz_out, stream);
+}
+
+int calibatt_validate_skiplist(const int32_t* kv_offsets, const int32_t* kv_indices, int64_t nnz,
+                               int32_t heads, int32_t n_blocks) {
+  const char* fn = "calibatt_validate_skiplist";
+  if (heads < 0 || n_blocks < 0 || nnz < 0)
+    return fail(CALIBATT_ERR_INVALID_ARG, "%s: negative size", fn);
+  if (!kv_offsets || (nnz > 0 && !kv_indices))
+    return fail(CALIBATT_ERR_INVALID_ARG, "%s: null pointer", fn);
+  const int64_t rows = (int64_t)heads * n_blocks;
+  if (kv_offsets[0] != 0) return fail(CALIBATT_ERR_BAD_SKIPLIST, "%s: offsets[0] = %d", fn, kv_offsets[0]);
+  if (kv_offsets[rows] != nnz)
+    return fail(CALIBATT_ERR_BAD_SKIPLIST, "%s: offsets[%lld] = %d != nnz %lld", fn,
+                (long long)rows, kv_offsets[rows], (long long)nnz);
+  for (int64_t r = 0; r < rows; ++r) {
+    const int32_t b = kv_offsets[r], e = kv_offsets[r + 1];
+    if (e < b) return fail(CALIBATT_ERR_BAD_SKIPLIST, "%s: row %lld: offsets decrease", fn, (long long)r);
+    if (e - b > n_blocks)
+      return fail(CALIBATT_ERR_BAD_SKIPLIST, "%s: row %lld: %d entries > R", fn, (long long)r, e - b);
+    for (int32_t i = b; i < e; ++i) {
+      const int32_t c = kv_indices[i];
+      if (c < 0 || c >= n_blocks)
+        return fail(CALIBATT_ERR_BAD_SKIPLIST, "%s: row %lld: index %d out of [0, %d)", fn,
+                    (long long)r, c, n_blocks);
+      if (i > b && c <= kv_indices[i - 1])
+        return fail(CALIBATT_ERR_BAD_SKIPLIST, "%s: row %lld: indices not ascending", fn, (long long)r);
+    }
+  }
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,158 @@
+// Device-side building blocks shared by the attention and energy kernels
+// (gfx950, wave64). Internal header: not part of the C ABI.
+//
+// Tile geometry. A workgroup of 256 threads (4 waves) owns one 128-row query
+// tile; wave w owns rows 32w..32w+31. Scores are computed transposed,
+// S^T = K Q^T, with v_mfma_f32_32x32x16_bf16 so that every lane ends up
+// holding one query row (lane % 32) and 64 of the 128 key columns of a block
+// (the other 64 live in lane ^ 32). Row max / sum then need a single
+// cross-lane exchange, and the softmax rescale of the output accumulator is a
+// per-lane scalar.
+//
+// 32x32 MFMA accumulator layout (16 fp32 per lane): lane l, element i holds
+// row 8*(i/4) + 4*(l/32) + (i%4), column l%32. A-operand lane l supplies row
+// l%32 and B-operand lane l supplies column l%32, each with an 8-element
+// k-slot chosen by l/32; since both operands of a product are loaded with
+// the same (lane group, element) -> k mapping, the sum over k is the same
+// whatever order the hardware contracts them in.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace calibatt {
+
+constexpr int kBlock = 128;       // tokens per block (B)
+constexpr int kDim = 128;         // head dimension (D)
+constexpr int kThreads = 256;     // 4 waves
+constexpr int kLdsStride = 136;   // bf16 per LDS tile row: 256 B + 16 B pad
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Work-item order across XCDs. Workgroups are dispatched round-robin over
+// the 8 XCDs (workgroup i -> XCD i % 8). Inside every run of 8*S workgroup
+// ids this map hands each XCD S consecutive work items, so the tiles that
+// share an XCD's L2 at a given time are neighbouring query blocks of one
+// head and reuse the same key/value blocks. The last partial run is left in
+// order.
+__device__ __forceinline__ int xcd_remap(int id, int n_items) {
+  constexpr int kXcd = 8, kPer = 32, kSpan = kXcd * kPer;
+  const int base = (id / kSpan) * kSpan;
+  if (base + kSpan > n_items) return id;
+  const int local = id - base;
+  return base + (local % kXcd) * kPer + local / kXcd;
+}
+
+__device__ __forceinline__ u32x4 load16(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+// Copies the 128 x 128 key tile starting at token key0 into LDS, row-major
+// with a padded row stride; rows at or past n_tokens are zero.
+__device__ __forceinline__ void stage_rows(uint16_t* __restrict__ lds,
+                                           const uint16_t* __restrict__ src,
+                                           int64_t stride_token, int key0,
+                                           int n_tokens, int tid) {
+  u32x4 buf[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int idx = tid + kThreads * j;
+    const int row = idx >> 4, ch = idx & 15;
+    const bool ok = key0 + row < n_tokens;
+    buf[j] = ok ? load16(src + (int64_t)(key0 + row) * stride_token + ch * 8)
+                : u32x4{0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int idx = tid + kThreads * j;
+    const int row = idx >> 4, ch = idx & 15;
+    *reinterpret_cast<u32x4*>(lds + row * kLdsStride + ch * 8) = buf[j];
+  }
+}
+
+// Copies the 128 x 128 value tile starting at token key0 into LDS transposed
+// ([d][key]) so that the P.V product can read 8 keys of one d as one 16-byte
+// LDS load. Inside every group of 16 keys the order is
+//   keys 0-3, 8-11, 4-7, 12-15,
+// which puts the 8 keys that MFMA lane group g needs for one k-step
+// (4g..4g+3 and 8+4g..8+4g+3, see attention kernel) side by side.
+// Thread t handles keys 4*(t%32) .. +3 and d range 16*(t/32) .. +15.
+__device__ __forceinline__ void stage_values_transposed(uint16_t* __restrict__ lds,
+                                                        const uint16_t* __restrict__ src,
+                                                        int64_t stride_token, int key0,
+                                                        int n_tokens, int tid) {
+  const int kg = tid & 31, dc = tid >> 5;
+  u32x4 vr[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int key = key0 + 4 * kg + i;
+    const bool ok = key < n_tokens;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      vr[i][h] = ok ? load16(src + (int64_t)key * stride_token + 16 * dc + 8 * h)
+                    : u32x4{0u, 0u, 0u, 0u};
+  }
+  const int a = kg & 3;
+  const int pos = (kg >> 2) * 16 + ((a & 1) << 3) + ((a & 2) << 1);
+#pragma unroll
+  for (int dd = 0; dd < 16; ++dd) {
+    const int h = dd >> 3, w = (dd & 7) >> 1;
+    const int sh = (dd & 1) * 16;
+    const uint32_t e0 = (vr[0][h][w] >> sh) & 0xffffu;
+    const uint32_t e1 = (vr[1][h][w] >> sh) & 0xffffu;
+    const uint32_t e2 = (vr[2][h][w] >> sh) & 0xffffu;
+    const uint32_t e3 = (vr[3][h][w] >> sh) & 0xffffu;
+    u32x2 out = {e0 | (e1 << 16), e2 | (e3 << 16)};
+    *reinterpret_cast<u32x2*>(lds + (16 * dc + dd) * kLdsStride + pos) = out;
+  }
+}
+
+// Query fragment (B operand of S^T = K Q^T) for one lane: row `tok` of q,
+// d = 16*s + 8*g .. +7 for s = 0..7. Zero when !valid.
+__device__ __forceinline__ void load_query(bf16x8 (&qf)[8], const uint16_t* __restrict__ q,
+                                           int64_t stride_token, int64_t tok, bool valid,
+                                           int g) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    u32x4 w = valid ? load16(q + tok * stride_token + 16 * s + 8 * g) : u32x4{0u, 0u, 0u, 0u};
+    qf[s] = __builtin_bit_cast(bf16x8, w);
+  }
+}
+
+// S^T for one wave: sacc[t] holds keys 32t..32t+31 (rows) x the wave's 32
+// queries (columns). Keys come from the LDS tile written by stage_rows.
+__device__ __forceinline__ void scores_transposed(f32x16 (&sacc)[4], const uint16_t* __restrict__ sK,
+                                                  const bf16x8 (&qf)[8], int l32, int g) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) sacc[t] = f32x16{};
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sK + (32 * t + l32) * kLdsStride + 16 * s + 8 * g);
+      sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[t], 0, 0, 0);
+    }
+  }
+}
+
+// Key (0..127 inside the block) held by accumulator element i of tile t.
+__device__ __forceinline__ int acc_key(int t, int i, int g) {
+  return 32 * t + 8 * (i >> 2) + 4 * g + (i & 3);
+}
+
+// Sets scores of keys at or past n_tokens to -inf (ragged last block).
+__device__ __forceinline__ void mask_ragged_keys(f32x16 (&sacc)[4], int key0, int n_tokens, int g) {
+  if (key0 + kBlock <= n_tokens) return;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (key0 + acc_key(t, i, g) >= n_tokens) sacc[t][i] = -__builtin_inff();
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace calibatt

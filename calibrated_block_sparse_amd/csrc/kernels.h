@@ -1,0 +1,62 @@
+// Kernel argument blocks and launchers (internal; the public interface is
+// include/calibatt.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace calibatt {
+
+constexpr int kMaxHeadsPerLaunch = 256;
+
+struct AttnArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  int64_t stride_head;
+  int64_t stride_token;
+  const int32_t* offsets;
+  const int32_t* indices;
+  int64_t nnz;
+  float scale_log2;          // softmax scale * log2(e)
+  int32_t n_tokens;
+  int32_t n_blocks;
+  int32_t n_rep;             // repeat heads in this launch (listed first in heads[])
+  int32_t n_sparse;          // non-repeat heads in this launch
+  int32_t rep_tiles;         // query tiles per repeat head
+  int32_t n_items;           // n_rep * rep_tiles + n_sparse * n_blocks
+  int32_t frames, rows, cols, anchors;
+  int32_t anchor_queries;    // frames * anchors * cols
+  int32_t heads[kMaxHeadsPerLaunch];
+};
+
+struct EnergyArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  int64_t stride_head;
+  int64_t stride_token;
+  float* row_max;            // [heads][R*128], log2 units
+  float* row_sum;            // [heads][R*128]
+  float* energy;             // [heads][R][R]
+  float scale_log2;
+  int32_t n_tokens;
+  int32_t n_blocks;
+  int32_t heads;
+};
+
+hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_block_energy(const EnergyArgs& a, hipStream_t stream);
+
+hipError_t launch_select_votes(const float* energy, int32_t n_draws, int32_t heads,
+                               int32_t n_blocks, uint64_t eps_fx, uint8_t* votes,
+                               int32_t* n_sel, hipStream_t stream);
+// mode 0: count nonzero mask entries; mode 1: binarise votes into mask, then count.
+hipError_t launch_row_counts(const uint8_t* src, int32_t rows, int32_t n_blocks, int mode,
+                             int32_t n_prompts, int32_t rho_num, int32_t rho_den,
+                             uint8_t* mask_out, int32_t* offsets, hipStream_t stream);
+hipError_t launch_offsets_scan(int32_t* offsets, int32_t rows, hipStream_t stream);
+hipError_t launch_compact(const uint8_t* mask, int32_t rows, int32_t n_blocks,
+                          const int32_t* offsets, int32_t* indices, hipStream_t stream);
+
+}  // namespace calibatt

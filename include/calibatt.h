@@ -1,0 +1,206 @@
+/*
+ * calibatt.h - C ABI of the MI355X (gfx950) calibrated block-sparse attention
+ * library (libcalibatt.so).
+ *
+ * The method (CalibAtt) is described on the page "让视频生成快 1.58 倍，却不改一行
+ * 模型代码：CalibAtt 的"注意力考古学"" (zhichai.net), cited here as [CalibAtt blog],
+ * and in the abstract of "Accelerating Text-to-Video Generation with
+ * Calibrated Sparse Attention", cited as [abstract].
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Block size B = 128 tokens and head dimension D = 128 are fixed
+ *   ([CalibAtt blog] §二 observation 1). R = ceil(N / 128) blocks per
+ *   sequence; when N is not a multiple of 128 the last block is ragged: keys
+ *   at or past N take no part in any softmax and query rows past N are
+ *   never written.
+ * - Tensors are bf16 (raw 16-bit storage, passed as void*), laid out as
+ *   [heads][N][D] with element strides stride_head and stride_token; D is
+ *   contiguous. Base pointers must be 16-byte aligned and both strides
+ *   multiples of 8 elements. Batch is folded into heads.
+ * - Every pointer named "device" is device memory owned by the caller. The
+ *   library allocates nothing and keeps no state between calls except the
+ *   thread-local error string.
+ * - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *   and is asynchronous unless an entry point says otherwise. Argument
+ *   errors are reported before anything is enqueued; launch failures return
+ *   CALIBATT_ERR_HIP. Nothing throws across this interface.
+ * - Calls that overlap on one device and write the same memory race.
+ */
+#ifndef CALIBATT_H
+#define CALIBATT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  CALIBATT_OK = 0,
+  CALIBATT_ERR_INVALID_ARG = -1,  /* null pointer, bad size, bad alignment */
+  CALIBATT_ERR_UNSUPPORTED = -2,  /* D != 128, sizes beyond the limits below */
+  CALIBATT_ERR_BAD_SKIPLIST = -3, /* malformed kept-block list (validators) */
+  CALIBATT_ERR_WORKSPACE = -4,    /* workspace missing or too small */
+  CALIBATT_ERR_HIP = -5           /* a HIP runtime call or launch failed */
+};
+
+#define CALIBATT_BLOCK 128
+#define CALIBATT_HEAD_DIM 128
+#define CALIBATT_MAX_BLOCKS 2047 /* R limit of the selection kernels */
+
+/* Latent video grid of a sequence: token n = f*rows*cols + y*cols + x
+ * (frame-major, row-major inside a frame; [CalibAtt blog] §六). `anchors`
+ * is k, the number of anchor rows a repeat head computes per frame. */
+typedef struct calibatt_grid {
+  int32_t frames;
+  int32_t rows;
+  int32_t cols;
+  int32_t anchors;
+} calibatt_grid;
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* calibatt_last_error(void);
+
+/* Interface version (increments on any change of this header). */
+int32_t calibatt_abi_version(void);
+
+/*
+ * Block-sparse attention forward with optional repeat heads.
+ *
+ * Non-repeat head h: for each query block r, attend only to the key blocks
+ * kv_indices[kv_offsets[h*R + r] .. kv_offsets[h*R + r + 1]) and skip all
+ * others ([CalibAtt blog] §三 online inference: a precomputed skip list tells
+ * the kernel which blocks to compute; [abstract]: selected connections are
+ * computed densely, unselected ones skipped). The result equals softmax
+ * attention with the logits of skipped blocks at -inf; a query block with an
+ * empty list gets zeros. Lists should be ascending; the order only affects
+ * rounding.
+ *
+ * Repeat head h (repeat_flags[h] != 0; [CalibAtt blog] §二 observation 4,
+ * §三): only the `anchors` anchor rows of every frame are computed, densely
+ * over all N keys, and each output token (f, y, x) receives the output of
+ * query (f, a(y), x), where A(m) = floor((2m+1)*rows / (2*anchors)) and
+ * a(y) = A(floor(y*anchors / rows)). Its CSR rows are ignored.
+ *
+ *   q, k, v      device bf16 [heads][N][128] (strides as above), inputs
+ *   o            device bf16, same layout and strides, output
+ *   scale        softmax scale (> 0), e.g. 1/sqrt(128)
+ *   kv_offsets   device int32 [heads*R + 1], non-decreasing, first 0
+ *   kv_indices   device int32 [nnz], key block indices in [0, R)
+ *   nnz          number of entries of kv_indices. Ranges are clamped to
+ *                [0, nnz) and indices outside [0, R) are skipped, so a
+ *                malformed list cannot read out of bounds; its result is
+ *                unspecified (check lists with calibatt_validate_skiplist).
+ *   repeat_flags host uint8 [heads] or NULL (no repeat heads)
+ *   grid         host pointer, required iff a repeat flag is set:
+ *                frames*rows*cols == N and 1 <= anchors <= rows
+ * kv_offsets / kv_indices may be NULL when every head repeats.
+ * heads == 0 or N == 0 is a no-op.
+ */
+int calibatt_sparse_attn_fwd(const void* q, const void* k, const void* v, void* o,
+                             int32_t heads, int32_t n_tokens, int32_t head_dim,
+                             int64_t stride_head, int64_t stride_token, float scale,
+                             const int32_t* kv_offsets, const int32_t* kv_indices,
+                             int64_t nnz, const uint8_t* repeat_flags,
+                             const calibatt_grid* grid, void* stream);
+
+/*
+ * Bytes of device workspace calibatt_block_energy needs (row statistics:
+ * two fp32 values per padded query row).
+ */
+size_t calibatt_block_energy_workspace(int32_t heads, int32_t n_tokens);
+
+/*
+ * Block energy of the post-softmax attention ([CalibAtt blog] §三 offline
+ * calibration, steps 1-2): with P = softmax(scale * Q K^T) over all N keys,
+ *   energy[h][r][c] = (1/|I_r|) * sum_{i in I_r} sum_{j in J_c} P_ij,
+ * where I_r, J_c are the query / key tokens of blocks r, c (|I_r| = 128
+ * except on a ragged last block-row, so every block-row sums to one).
+ *
+ *   q, k       device bf16 [heads][N][128], strides as above
+ *   energy     device fp32 [heads][R][R], output (dense, row-major)
+ *   workspace  device, >= calibatt_block_energy_workspace(heads, N) bytes
+ */
+int calibatt_block_energy(const void* q, const void* k, float* energy,
+                          int32_t heads, int32_t n_tokens, int32_t head_dim,
+                          int64_t stride_head, int64_t stride_token, float scale,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Threshold eps(t) = A + (C - A) * exp(-k * t / T) ([CalibAtt blog] §三)
+ * as an integer multiple of 2^-40, rounded to nearest (ties to even).
+ * Host function, synchronous.
+ */
+uint64_t calibatt_eps_fx(double t, double T, double A, double C, double k);
+
+/*
+ * Greedy selection and vote accumulation ([CalibAtt blog] §三 offline
+ * calibration step 3 and the mean over prompts). For every draw p, head h
+ * and block-row r: energies are rounded to multiples of 2^-40 (nearest,
+ * ties to even), ordered by energy descending and column ascending, and the
+ * shortest prefix whose integer sum reaches eps_fx (>=) is selected (the
+ * whole row if none does). votes[h][r][c] is incremented by one for every
+ * selected block, saturating at 255.
+ *
+ *   energy   device fp32 [n_draws][heads][R][R], input
+ *   eps_fx   threshold in units of 2^-40 (see calibatt_eps_fx)
+ *   votes    device uint8 [heads][R][R], read and updated in place
+ *   n_sel    device int32 [n_draws][heads][R] (selected count n*) or NULL
+ * 1 <= R <= CALIBATT_MAX_BLOCKS.
+ */
+int calibatt_build_mask(const float* energy, int32_t n_draws, int32_t heads,
+                        int32_t n_blocks, uint64_t eps_fx, uint8_t* votes,
+                        int32_t* n_sel, void* stream);
+
+/*
+ * Binarise averaged votes and compile kept-block lists ([CalibAtt blog] §三:
+ * M_bar = votes / |D| binarised at rho; §三 online inference: static skip
+ * list per (timestep, layer, head)). Keeps (r, c) iff
+ * votes * rho_den >= rho_num * n_prompts; a block-row left empty keeps its
+ * most-voted column (lowest index on ties). Then compiles as
+ * calibatt_compile_skiplist.
+ *
+ *   votes       device uint8 [heads][R][R]
+ *   n_prompts   |D|, 1..255; rho = rho_num / rho_den with 0 <= rho_num <= rho_den, rho_den >= 1
+ *   mask        device uint8 [heads][R][R], output (0/1)
+ *   kv_offsets  device int32 [heads*R + 1], output
+ *   kv_indices  device int32, capacity heads*R*R, output
+ *   nnz_out     host int64* or NULL. When non-NULL the call waits for the
+ *               stream and stores the number of kept blocks.
+ */
+int calibatt_finalize_mask(const uint8_t* votes, int32_t heads, int32_t n_blocks,
+                           int32_t n_prompts, int32_t rho_num, int32_t rho_den,
+                           uint8_t* mask, int32_t* kv_offsets, int32_t* kv_indices,
+                           int64_t* nnz_out, void* stream);
+
+/*
+ * Compile a block mask into per-query-block kept lists (CSR): row h*R + r
+ * lists the columns c with mask[h][r][c] != 0 in ascending order.
+ *
+ *   mask        device uint8 [heads][R][R]
+ *   kv_offsets  device int32 [heads*R + 1], output
+ *   kv_indices  device int32, capacity heads*R*R, output
+ *   nnz_out     as for calibatt_finalize_mask
+ * heads*R*R must be below 2^31.
+ */
+int calibatt_compile_skiplist(const uint8_t* mask, int32_t heads, int32_t n_blocks,
+                              int32_t* kv_offsets, int32_t* kv_indices,
+                              int64_t* nnz_out, void* stream);
+
+/*
+ * Check a kept-block list held in HOST memory: offsets[0] == 0,
+ * non-decreasing, offsets[heads*R] == nnz, every index in [0, R) and
+ * strictly ascending within a row. Returns CALIBATT_OK or
+ * CALIBATT_ERR_BAD_SKIPLIST (message names the first offending row).
+ * Synchronous, touches no device.
+ */
+int calibatt_validate_skiplist(const int32_t* kv_offsets, const int32_t* kv_indices,
+                               int64_t nnz, int32_t heads, int32_t n_blocks);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CALIBATT_H */

@@ -1,0 +1,128 @@
+"""The C ABI on the host: the shared library loads, exports every function
+include/calibatt.h declares, and rejects bad arguments before touching a
+device. No GPU is needed."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import calibrated_block_sparse_amd as cbs
+import oracle
+from synth import CALIB_WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "calibatt.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return cbs.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(calibatt_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(cbs.SIGNATURES), "binding and header disagree"
+
+
+def test_abi_version(lib):
+    assert cbs.calibatt_abi_version() == 1
+
+
+def fake(n=16):
+    return ctypes.c_void_p(n * 4096)  # non-null, aligned; never dereferenced here
+
+
+def attn(lib, **kw):
+    args = dict(q=fake(), k=fake(), v=fake(), o=fake(), heads=2, n=1024, d=128, sh=1024 * 128,
+                stok=128, scale=0.088, off=fake(), idx=fake(), nnz=10, flags=None, grid=None)
+    args.update(kw)
+    return lib.calibatt_sparse_attn_fwd(args["q"], args["k"], args["v"], args["o"], args["heads"],
+                                        args["n"], args["d"], args["sh"], args["stok"], args["scale"],
+                                        args["off"], args["idx"], args["nnz"], args["flags"],
+                                        args["grid"], None)
+
+
+def test_attention_argument_errors(lib):
+    assert attn(lib, d=64) == -2
+    assert "head_dim" in cbs.calibatt_last_error()
+    assert attn(lib, q=None) == -1
+    assert attn(lib, q=ctypes.c_void_p(4096 + 2)) == -1
+    assert attn(lib, stok=100) == -1
+    assert attn(lib, scale=0.0) == -1
+    assert attn(lib, scale=float("nan")) == -1
+    assert attn(lib, nnz=-1) == -1
+    assert attn(lib, off=None) == -1
+    assert attn(lib, heads=-1) == -1
+    flags = (ctypes.c_uint8 * 2)(0, 1)
+    assert attn(lib, flags=flags) == -1                        # repeat head without grid
+    g = cbs.Grid(2, 16, 30, 5)                                 # 960 != 1024 tokens
+    assert attn(lib, flags=flags, grid=ctypes.byref(g)) == -1
+    g = cbs.Grid(2, 16, 32, 17)                                # anchors > rows
+    assert attn(lib, flags=flags, grid=ctypes.byref(g)) == -1
+    # empty problems are no-ops and succeed
+    assert attn(lib, heads=0) == 0 and attn(lib, n=0) == 0
+
+
+def test_energy_argument_errors(lib):
+    ws = cbs.calibatt_block_energy_workspace(2, 1000)
+    assert ws == 2 * 4 * 2 * 8 * 128
+    f = lambda **kw: lib.calibatt_block_energy(kw.get("q", fake()), fake(), kw.get("e", fake()),
+                                               2, kw.get("n", 1000), kw.get("d", 128), 1000 * 128,
+                                               128, 0.1, kw.get("ws", fake()), kw.get("wsb", ws), None)
+    assert f(d=96) == -2
+    assert f(q=None) == -1
+    assert f(wsb=ws - 1) == -4
+    assert f(ws=None) == -4
+    assert f(n=2048 * 128) == -2                               # R beyond the selection limit
+
+
+def test_mask_argument_errors(lib):
+    assert lib.calibatt_build_mask(fake(), 1, 1, 2048, 5, fake(), None, None) == -2
+    assert lib.calibatt_build_mask(None, 1, 1, 8, 5, fake(), None, None) == -1
+    assert lib.calibatt_build_mask(fake(), 0, 1, 8, 5, fake(), None, None) == 0
+    fin = lambda n, rn, rd: lib.calibatt_finalize_mask(fake(), 1, 8, n, rn, rd, fake(), fake(),
+                                                       fake(), None, None)
+    assert fin(0, 1, 2) == -1 and fin(256, 1, 2) == -1 and fin(64, 3, 2) == -1 and fin(64, 1, 0) == -1
+    assert lib.calibatt_compile_skiplist(fake(), 40, 8000, fake(), fake(), None, None) == -2
+
+
+def test_eps_fx_matches_oracle(lib):
+    w = CALIB_WORKLOADS["calibration_480p"]
+    for t in list(w.steps) + list(range(0, 50, 7)):
+        eps = oracle.eps_schedule(t, w.total_steps, w.eps_floor, w.eps_start, w.eps_rate)
+        assert cbs.calibatt_eps_fx(t, w.total_steps, w.eps_floor, w.eps_start, w.eps_rate) == oracle.eps_fx(eps)
+    # LightX2V-style 4-step schedule
+    for t in range(4):
+        eps = oracle.eps_schedule(t, 4, 0.84, 0.99, 5.0)
+        assert cbs.calibatt_eps_fx(t, 4, 0.84, 0.99, 5.0) == oracle.eps_fx(eps)
+
+
+def test_validate_skiplist_host(lib):
+    rng = np.random.Generator(np.random.PCG64(3))
+    m = (rng.random((3, 9, 9)) < 0.4).astype(np.uint8)
+    off, idx = oracle.compile_skiplist(m)
+    cbs.calibatt_validate_skiplist(off, idx, 3, 9)
+    bad = [
+        (off, np.where(idx == idx.max(), 9, idx)),             # index out of range
+        (off, idx[::-1].copy()),                               # not ascending
+        (np.r_[1, off[1:]], idx),                              # offsets[0] != 0
+    ]
+    o2 = off.copy()
+    o2[5] = o2[4] - 1                                          # decreasing offsets
+    bad.append((o2, idx))
+    for o, i in bad:
+        with pytest.raises(cbs.CalibAttError) as e:
+            cbs.calibatt_validate_skiplist(o, i, 3, 9)
+        assert e.value.code == -3

@@ -1,0 +1,204 @@
+"""GPU parity of calibatt_sparse_attn_fwd (through the C ABI) against the fp64
+oracle on the same seeded bf16 inputs.
+
+Bar: max-abs <= 2e-2 and relative Frobenius <= 1e-2 on every compared
+output; kept-block lists bit-exact against the oracle's compilation.
+Small cases compare every output; the full Wan / Mochi layer shapes compare
+all heads on the first, the ragged last and seeded query blocks (and
+sampled tokens of repeat heads)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import (ATTN_WORKLOADS, VideoGrid, bernoulli_mask, bf16_bits, block_mask,
+                   gaussian_bf16, n_blocks, qkv, repeat_flags)
+from tests._util import assert_attn_close, f64, say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def run(cbs, q, k, v, mask_np, scale, flags=None, grid=None):
+    mask = torch.from_numpy(mask_np).to(DEV)
+    off, idx = cbs.compile_skiplist(mask)
+    o = cbs.sparse_attention(q, k, v, off, idx, scale, flags, grid)
+    torch.cuda.synchronize()
+    return o, off, idx
+
+
+def oracle_head_blocks(q, k, v, mask, scale, h, blocks):
+    qb, kb, vb = (bf16_bits(t[h]) for t in (q, k, v))
+    return [oracle.block_sparse_attention_block(qb, kb, vb, scale, np.flatnonzero(mask[h, r]), r)
+            for r in blocks]
+
+
+def full_compare(cbs, q, k, v, mask, scale, what):
+    o, off, idx = run(cbs, q, k, v, mask, scale)
+    H, N, _ = q.shape
+    R = n_blocks(N)
+    for h in range(H):
+        got = f64(o[h])
+        want = np.concatenate(oracle_head_blocks(q, k, v, mask, scale, h, range(R)))
+        e = assert_attn_close(got, want, f"{what} head {h}")
+        say(f"  {what} head {h}: max-abs {e[0]:.2e} rel-fro {e[1]:.2e}")
+    return o, off, idx
+
+
+def test_single_head_1k(gpu):
+    w = ATTN_WORKLOADS["single_head_1k"]
+    say("case single_head_1k")
+    q, k, v = (t.to(DEV) for t in qkv(w))
+    mask = block_mask(w)
+    _, off, idx = full_compare(gpu, q, k, v, mask, w.scale, "single_head_1k")
+    o_off, o_idx = oracle.compile_skiplist(mask)
+    assert np.array_equal(off.cpu().numpy(), o_off) and np.array_equal(idx.cpu().numpy(), o_idx)
+
+
+@pytest.mark.parametrize("N,H,seed", [(1000, 3, 1), (130, 2, 2), (128, 1, 3), (7, 1, 4), (2944, 2, 5)])
+def test_ragged_and_tiny(gpu, N, H, seed):
+    say(f"case ragged N={N} H={H}")
+    q, k, v = (gaussian_bf16(seed * 10 + i, (H, N, 128)).to(DEV) for i in range(3))
+    R = n_blocks(N)
+    mask = bernoulli_mask(seed, H, R, 0.5, diagonal=True)
+    if R > 2:
+        mask[0, 1, :] = 0          # an empty kept list -> zeros
+    o, _, _ = full_compare(gpu, q, k, v, mask, 1 / np.sqrt(128), f"N={N}")
+    if R > 2:
+        assert not f64(o[0, 128:256]).any()
+
+
+def test_peaky_scores(gpu):
+    """Scaled-up queries make softmax rows concentrated, so the tolerance
+    bites on large outputs."""
+    say("case peaky")
+    N, H = 1024, 2
+    q = gaussian_bf16(71, (H, N, 128), std=4.0).to(DEV)
+    k, v = (gaussian_bf16(72 + i, (H, N, 128)).to(DEV) for i in range(2))
+    mask = bernoulli_mask(73, H, 8, 0.4)
+    full_compare(gpu, q, k, v, mask, 1 / np.sqrt(128), "peaky")
+
+
+def test_all_kept_is_dense(gpu):
+    say("case all-kept")
+    N, H = 1000, 2
+    q, k, v = (gaussian_bf16(80 + i, (H, N, 128), std=2.0).to(DEV) for i in range(3))
+    o, _, _ = run(gpu, q, k, v, np.ones((H, 8, 8), np.uint8), 0.1)
+    for h in range(H):
+        want = oracle.dense_attention(*(bf16_bits(t[h]) for t in (q, k, v)), 0.1)
+        assert_attn_close(f64(o[h]), want, "all-kept")
+
+
+def test_skipped_blocks_do_not_matter_bitwise(gpu):
+    say("case skipped-blocks")
+    N, H = 1024, 2
+    q, k, v = (gaussian_bf16(90 + i, (H, N, 128)).to(DEV) for i in range(3))
+    mask = bernoulli_mask(93, H, 8, 0.5)
+    o1, _, _ = run(gpu, q, k, v, mask, 0.09)
+    k2, v2 = k.clone(), v.clone()
+    for h in range(H):
+        skipped_everywhere = [c for c in range(8) if not mask[h, :, c].any()]
+        for c in skipped_everywhere:
+            k2[h, c * 128:(c + 1) * 128] = 7.0
+            v2[h, c * 128:(c + 1) * 128] = -3.0
+    # Perturb a block that row 0 skips but others keep: only rows keeping it may change.
+    c_pert = int(np.flatnonzero(mask[0, 0] == 0)[0])
+    k2[0, c_pert * 128:(c_pert + 1) * 128] += 1.0
+    o2, _, _ = run(gpu, q, k2, v2, mask, 0.09)
+    assert torch.equal(o1[1], o2[1])
+    for r in range(8):
+        if not mask[0, r, c_pert]:
+            assert torch.equal(o1[0, r * 128:(r + 1) * 128], o2[0, r * 128:(r + 1) * 128])
+
+
+def test_deterministic(gpu):
+    say("case deterministic")
+    N, H = 2000, 4
+    q, k, v = (gaussian_bf16(100 + i, (H, N, 128)).to(DEV) for i in range(3))
+    mask = bernoulli_mask(103, H, n_blocks(N), 0.6)
+    o1, _, _ = run(gpu, q, k, v, mask, 0.09)
+    o2, _, _ = run(gpu, q, k, v, mask, 0.09)
+    assert torch.equal(o1, o2)
+
+
+def test_strided_layout(gpu):
+    """[N][H][D] interleaved storage (stride_token = H*D) gives the same
+    result as contiguous [H][N][D]."""
+    say("case strided")
+    N, H = 700, 3
+    base = [gaussian_bf16(110 + i, (N, H, 128)).to(DEV) for i in range(3)]
+    views = [t.permute(1, 0, 2) for t in base]
+    mask = bernoulli_mask(113, H, n_blocks(N), 0.5)
+    m = torch.from_numpy(mask).to(DEV)
+    off, idx = gpu.compile_skiplist(m)
+    o_view = torch.empty_like(base[0]).permute(1, 0, 2)
+    gpu.calibatt_sparse_attn_fwd(*views, o_view, off, idx, 0.09)
+    o_cont = gpu.sparse_attention(*(t.contiguous() for t in views), off, idx, 0.09)
+    torch.cuda.synchronize()
+    assert torch.equal(o_view.contiguous(), o_cont)
+
+
+@pytest.mark.parametrize("F,Hs,W,kk", [(2, 30, 7, 5), (3, 45, 4, 5), (2, 10, 13, 10), (1, 7, 9, 3)])
+def test_repeat_heads_small(gpu, F, Hs, W, kk):
+    say(f"case repeat grid {F}x{Hs}x{W} k={kk}")
+    N = F * Hs * W
+    H = 3
+    q, k, v = (gaussian_bf16(120 + i, (H, N, 128), std=1.5).to(DEV) for i in range(3))
+    R = n_blocks(N)
+    mask = bernoulli_mask(124, H, R, 0.5)
+    flags = np.array([0, 1, 1], np.uint8)
+    o, _, _ = run(gpu, q, k, v, mask, 0.09, flags, (F, Hs, W, kk))
+    want0 = oracle.block_sparse_attention(*(bf16_bits(t[0]) for t in (q, k, v)), 0.09, mask[0])
+    assert_attn_close(f64(o[0]), want0, "non-repeat head")
+    for h in (1, 2):
+        want = oracle.repeat_head_attention(*(bf16_bits(t[h]) for t in (q, k, v)), 0.09, F, Hs, W, kk)
+        assert_attn_close(f64(o[h]), want, f"repeat head {h}")
+        # copies are exact: every row equals its anchor row bit for bit
+        og = o[h].view(F, Hs, W, 128)
+        arow = oracle.anchor_of_row(Hs, kk)
+        for y in range(Hs):
+            assert torch.equal(og[:, y], og[:, int(arow[y])])
+
+
+def sampled_blocks(R, seed, n=14):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    extra = rng.choice(np.arange(1, R - 1), size=min(n, R - 2), replace=False)
+    return sorted(set([0, R - 1, *extra.tolist()]))
+
+
+@pytest.mark.parametrize("name", ["wan21_480p_layer", "wan21_720p_layer", "mochi1_480p_layer"])
+def test_full_size_layer_sampled(gpu, name):
+    w = ATTN_WORKLOADS[name]
+    say(f"case full-size {name}: H={w.heads} N={w.n_tokens}")
+    q, k, v = qkv(w, device=DEV)
+    mask = block_mask(w)
+    flags = repeat_flags(w)
+    grid = (w.grid.frames, w.grid.rows, w.grid.cols, w.anchors) if flags.any() else None
+    o, off, idx = run(gpu, q, k, v, mask, w.scale, flags if flags.any() else None, grid)
+    R = w.n_blocks
+    kept = (mask.reshape(w.heads, -1).sum(1))
+    assert (kept == w.keep_per_head()).all()
+    o_off, o_idx = oracle.compile_skiplist(mask)
+    assert np.array_equal(off.cpu().numpy(), o_off) and np.array_equal(idx.cpu().numpy(), o_idx)
+    heads = range(w.heads)
+    n_samp = 6 if name == "wan21_720p_layer" else 8
+    for h in heads:
+        qb, kb, vb = (bf16_bits(t[h]) for t in (q, k, v))
+        if flags[h]:
+            rng = np.random.Generator(np.random.PCG64(1000 + h))
+            toks = np.r_[np.arange(128), rng.integers(0, w.n_tokens, 768), w.n_tokens - 1]
+            want = oracle.repeat_head_attention(qb, kb, vb, w.scale, w.grid.frames, w.grid.rows,
+                                                w.grid.cols, w.anchors, toks)
+            got = f64(o[h][torch.from_numpy(toks).to(DEV)])
+            assert_attn_close(got, want, f"{name} repeat head {h}")
+            continue
+        blocks = sampled_blocks(R, 500 + h, n_samp)
+        want = np.concatenate([oracle.block_sparse_attention_block(qb, kb, vb, w.scale,
+                                                                   np.flatnonzero(mask[h, r]), r)
+                               for r in blocks])
+        rows = np.concatenate([np.arange(r * 128, min(r * 128 + 128, w.n_tokens)) for r in blocks])
+        got = f64(o[h][torch.from_numpy(rows).to(DEV)])
+        e = assert_attn_close(got, want, f"{name} head {h}")
+        if h % 10 == 0:
+            say(f"  {name} head {h}: max-abs {e[0]:.2e} rel-fro {e[1]:.2e}")

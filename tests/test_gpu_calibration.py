@@ -1,0 +1,191 @@
+"""GPU parity of the calibration path (calibatt_block_energy,
+calibatt_build_mask, calibatt_finalize_mask, calibatt_compile_skiplist)
+against the oracle, through the C ABI.
+
+Bars: energies per element within 1e-4 relative + 1e-7 absolute and row L1
+within 1e-4; selections, selected counts, votes, masks and kept lists
+bit-exact when both sides start from the same fp32 energies; end to end
+(GPU energies vs oracle energies) selections may differ only on rows whose
+oracle prefix sums lie within 1e-4 of eps."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import (CALIB_WORKLOADS, bernoulli_mask, bf16_bits, calib_basis, calib_draw,
+                   energy_rows, gaussian_bf16, n_blocks)
+from tests._util import assert_energy_close, f64, say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def gpu_energy(cbs, q, k, scale):
+    e = cbs.block_energy(q, k, scale)
+    torch.cuda.synchronize()
+    return e
+
+
+@pytest.mark.parametrize("N,H,std", [(1024, 1, 1.0), (1024, 2, 4.0), (1000, 3, 2.0), (7, 1, 1.0),
+                                     (2944, 2, 3.0)])
+def test_energy_full(gpu, N, H, std):
+    say(f"case energy N={N} H={H} std={std}")
+    q = gaussian_bf16(200 + N, (H, N, 128), std=std).to(DEV)
+    k = gaussian_bf16(201 + N, (H, N, 128)).to(DEV)
+    e = f64(gpu_energy(gpu, q, k, 1 / np.sqrt(128)))
+    for h in range(H):
+        want = oracle.block_energy(bf16_bits(q[h]), bf16_bits(k[h]), 1 / np.sqrt(128))
+        assert_energy_close(e[h], want, f"energy head {h}")
+        np.testing.assert_allclose(e[h].sum(axis=1), 1.0, atol=1e-5)
+
+
+def test_energy_zero_queries_closed_form(gpu):
+    say("case energy Q=0")
+    N = 1000
+    q = torch.zeros(1, N, 128, dtype=torch.bfloat16, device=DEV)
+    k = gaussian_bf16(210, (1, N, 128)).to(DEV)
+    e = f64(gpu_energy(gpu, q, k, 0.1))[0]
+    want = np.array([128] * 7 + [104]) / N
+    np.testing.assert_allclose(e, np.broadcast_to(want, e.shape), rtol=1e-6)
+
+
+def test_energy_calibration_size_sampled(gpu):
+    """Calibration shape (40 heads, N = 32760 = 21 x 30 x 52), one draw,
+    block-rows sampled per head."""
+    w = CALIB_WORKLOADS["calibration_480p"]
+    say(f"case energy full-size H={w.heads} N={w.n_tokens}")
+    basis = calib_basis(w, DEV)
+    q, k = calib_draw(w, 0, basis, DEV)
+    e = gpu_energy(gpu, q, k, w.scale)
+    R = n_blocks(w.n_tokens)
+    assert np.allclose(f64(e).sum(axis=-1), 1.0, atol=1e-5)
+    rng = np.random.Generator(np.random.PCG64(7))
+    for h in range(0, w.heads, 4):
+        rows = sorted(set([0, R - 1, *rng.choice(R, 3, replace=False).tolist()]))
+        want = oracle.block_energy(bf16_bits(q[h]), bf16_bits(k[h]), w.scale, rows)
+        assert_energy_close(f64(e[h])[rows], want, f"energy head {h}")
+
+
+@pytest.mark.parametrize("kind", ["dirichlet", "peaky", "ties", "uniform", "onehot"])
+@pytest.mark.parametrize("R", [8, 64, 100, 591, 2047])
+def test_select_bit_exact(gpu, kind, R):
+    say(f"case select {kind} R={R}")
+    H = 2 if R < 1000 else 1
+    draws = 3 if R <= 591 else 1
+    E = np.stack([energy_rows(300 + 7 * d + R, H, R, kind) for d in range(draws)])
+    if R == 2047:
+        E = E[:, :, :64]  # 64 of the 2047 rows keep the case small
+        E = np.ascontiguousarray(E)
+    rows = E.shape[2]
+    for eps in (0.5, 0.84, 0.9, 0.99):
+        efx = gpu.calibatt_eps_fx(0, 1, eps, eps, 0)
+        assert efx == oracle.eps_fx(eps)
+        sel, nstar = oracle.greedy_select(E, efx)
+        want_votes = oracle.accumulate_votes(sel)
+        # The GPU takes [n_draws][H][R][R]; pad the row count to R with zero rows.
+        Ep = np.zeros((draws, H, R, R), np.float32)
+        Ep[:, :, :rows] = E
+        votes = torch.zeros(H, R, R, dtype=torch.uint8, device=DEV)
+        nsel = torch.zeros(draws, H, R, dtype=torch.int32, device=DEV)
+        gpu.calibatt_build_mask(torch.from_numpy(Ep).to(DEV), efx, votes, nsel)
+        torch.cuda.synchronize()
+        v = votes.cpu().numpy()[:, :rows]
+        assert np.array_equal(v, want_votes), f"votes differ (eps {eps})"
+        assert np.array_equal(nsel.cpu().numpy()[:, :, :rows], nstar), f"n* differ (eps {eps})"
+
+
+def test_votes_accumulate_and_saturate(gpu):
+    say("case votes saturate")
+    R, H = 16, 1
+    E = energy_rows(400, H, R, "peaky")
+    votes = torch.full((H, R, R), 250, dtype=torch.uint8, device=DEV)
+    efx = oracle.eps_fx(0.9)
+    Ed = torch.from_numpy(np.stack([E] * 10)).to(DEV)
+    gpu.calibatt_build_mask(Ed, efx, votes)
+    torch.cuda.synchronize()
+    sel, _ = oracle.greedy_select(E, efx)
+    want = np.minimum(250 + 10 * sel.astype(np.int64), 255)
+    assert np.array_equal(votes.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("H,R,n,rho", [(2, 8, 64, (1, 2)), (3, 100, 64, (1, 2)), (2, 591, 37, (3, 10)),
+                                       (1, 33, 1, (1, 2)), (2, 50, 255, (7, 10))])
+def test_finalize_bit_exact(gpu, H, R, n, rho):
+    say(f"case finalize H={H} R={R} n={n} rho={rho}")
+    rng = np.random.Generator(np.random.PCG64(R + n))
+    votes = rng.integers(0, n + 1, size=(H, R, R)).astype(np.uint8)
+    votes[0, 0] = 0                       # empty row -> fallback to column 0
+    votes[0, 1] = 0
+    votes[0, 1, R // 2] = 1 if n > 1 else 0  # below rho -> fallback to its argmax
+    if n == 64:
+        votes[-1, -1, :3] = [32, 31, 33]  # the rho tie is kept
+    want_mask = oracle.binarize(votes, n, *rho)
+    want_off, want_idx = oracle.compile_skiplist(want_mask)
+    vd = torch.from_numpy(votes).to(DEV)
+    mask = torch.empty_like(vd)
+    off = torch.empty(H * R + 1, dtype=torch.int32, device=DEV)
+    idx = torch.empty(H * R * R, dtype=torch.int32, device=DEV)
+    nnz = gpu.calibatt_finalize_mask(vd, n, rho[0], rho[1], mask, off, idx)
+    assert nnz == want_idx.size
+    assert np.array_equal(mask.cpu().numpy(), want_mask)
+    assert np.array_equal(off.cpu().numpy(), want_off)
+    assert np.array_equal(idx.cpu().numpy()[:nnz], want_idx)
+
+
+@pytest.mark.parametrize("H,R,p", [(40, 591, 0.375), (1, 1, 1.0), (3, 64, 0.0), (5, 2047, 0.01)])
+def test_compile_bit_exact(gpu, H, R, p):
+    say(f"case compile H={H} R={R}")
+    m = bernoulli_mask(500 + R, H, R, p, diagonal=False)
+    want_off, want_idx = oracle.compile_skiplist(m)
+    off, idx = gpu.compile_skiplist(torch.from_numpy(m).to(DEV))
+    assert np.array_equal(off.cpu().numpy(), want_off)
+    assert np.array_equal(idx.cpu().numpy(), want_idx)
+
+
+def test_calibration_end_to_end_small(gpu):
+    """Small calibration run: energies -> selections at eps(t) for three
+    steps -> votes over all draws -> binarised masks -> kept lists. GPU
+    (energies included) vs oracle; selections may differ only on rows whose
+    oracle prefix sums come within 1e-4 of eps."""
+    w = CALIB_WORKLOADS["calibration_small"]
+    say(f"case calibration small H={w.heads} N={w.n_tokens} draws={w.draws}")
+    R = n_blocks(w.n_tokens)
+    basis = calib_basis(w, "cpu")
+    votes_g = {t: torch.zeros(w.heads, R, R, dtype=torch.uint8, device=DEV) for t in w.steps}
+    votes_o = {t: np.zeros((w.heads, R, R), np.int64) for t in w.steps}
+    near = 0
+    for p in range(w.draws):
+        q, k = calib_draw(w, p, basis, "cpu")
+        e_g = gpu_energy(gpu, q.to(DEV), k.to(DEV), w.scale)
+        e_o = np.stack([oracle.block_energy(bf16_bits(q[h]), bf16_bits(k[h]), w.scale)
+                        for h in range(w.heads)])
+        assert_energy_close(f64(e_g), e_o, f"draw {p}")
+        for t in w.steps:
+            efx = gpu.calibatt_eps_fx(t, w.total_steps, w.eps_floor, w.eps_start, w.eps_rate)
+            nsel = torch.zeros(1, w.heads, R, dtype=torch.int32, device=DEV)
+            before = votes_g[t].clone()
+            gpu.calibatt_build_mask(e_g, efx, votes_g[t], nsel)
+            sel_g = (votes_g[t] - before).cpu().numpy()
+            sel_o, _ = oracle.greedy_select(e_o, efx)
+            votes_o[t] += sel_o
+            diff = np.flatnonzero((sel_g != sel_o).any(axis=-1).ravel())
+            srt = -np.sort(-e_o, axis=-1)
+            cs = np.cumsum(srt, axis=-1).reshape(-1, R)
+            eps = efx / 2.0 ** 40
+            for row in diff:
+                assert np.min(np.abs(cs[row] - eps)) < 1e-4, f"draw {p} t {t} row {row}"
+            near += diff.size
+    say(f"  rows differing near eps: {near}")
+    for t in w.steps:
+        vg = votes_g[t].cpu().numpy()
+        if near == 0:
+            assert np.array_equal(vg, votes_o[t])
+        mask = torch.empty(w.heads, R, R, dtype=torch.uint8, device=DEV)
+        off = torch.empty(w.heads * R + 1, dtype=torch.int32, device=DEV)
+        idx = torch.empty(w.heads * R * R, dtype=torch.int32, device=DEV)
+        nnz = gpu.calibatt_finalize_mask(votes_g[t], w.draws, *w.rho, mask, off, idx)
+        want = oracle.binarize(votes_o[t], w.draws, *w.rho)
+        same_rows = (vg == votes_o[t]).all(axis=-1)
+        assert np.array_equal(mask.cpu().numpy()[same_rows], want[same_rows])
+        say(f"  t={t}: kept fraction {nnz / (w.heads * R * R):.3f}")
