@@ -197,6 +197,9 @@ def main():
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calib-draws", type=int, default=4)
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense-mask run")
+    ap.add_argument("--copy-ref-mib", type=int, default=0,
+                    help="first run one plain device copy of this many MiB (counter reference)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
@@ -208,6 +211,14 @@ def main():
     import calibrated_block_sparse_amd as cbs
     cbs.load_library()
 
+    if args.copy_ref_mib:
+        n = args.copy_ref_mib * 2 ** 20 // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] reference copy of {args.copy_ref_mib} MiB done")
+        del src, dst
     log(f"[bench] {args.workload}: sparse mask, {args.steps} steps after {args.warmup} warmup")
     sp = attn_case(cbs, args.workload, args.steps, args.warmup)
     w = sp["workload"]
@@ -217,11 +228,13 @@ def main():
     eff = flop / (ms_step * 1e-3) / 1e12
     log(f"[bench] sparse: {ms_step:.3f} ms/step, {eff:.1f} TFLOP/s effective")
 
-    log("[bench] dense mask (every block kept)")
-    dn = attn_case(cbs, args.workload, max(3, args.steps // 4), 2, dense=True)
-    dense_ms = float(np.median(dn["per_ms"]))
-    dense_tflops = dn["pairs"] * PAIR_FLOP / (dense_ms * 1e-3) / 1e12
-    del dn
+    dense_ms = dense_tflops = None
+    if not args.no_dense:
+        log("[bench] dense mask (every block kept)")
+        dn = attn_case(cbs, args.workload, max(3, args.steps // 4), 2, dense=True)
+        dense_ms = float(np.median(dn["per_ms"]))
+        dense_tflops = dn["pairs"] * PAIR_FLOP / (dense_ms * 1e-3) / 1e12
+        del dn
 
     per_launch_ms = float(np.mean(sp["per_ms"]))
     achieved = flop / (per_launch_ms * 1e-3) / 1e12
@@ -241,8 +254,8 @@ def main():
         "config": {"workload": w.name, "heads": w.heads, "n_tokens": w.n_tokens,
                    "head_dim": w.head_dim, "block": 128, "block_sparsity": w.sparsity,
                    "kept_pairs": sp["pairs"], "frames_x_rows_x_cols": [w.grid.frames, w.grid.rows, w.grid.cols]},
-        "speedup_vs_dense_mask": round(dense_ms / ms, 3),
-        "dense_mask": {"ms": round(dense_ms, 3), "tflops": round(dense_tflops, 1)},
+        "speedup_vs_dense_mask": round(dense_ms / ms, 3) if dense_ms else None,
+        "dense_mask": {"ms": round(dense_ms, 3), "tflops": round(dense_tflops, 1)} if dense_ms else None,
         "sparse_ms_p10_p50_p90": [round(float(x), 4) for x in np.percentile(sp["per_ms"], [10, 50, 90])],
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),

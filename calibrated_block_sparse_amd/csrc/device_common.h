@@ -155,4 +155,70 @@ __device__ __forceinline__ void mask_ragged_keys(f32x16 (&sacc)[4], int key0, in
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ---------------------------------------------------------------------------
+// Asynchronous tile staging (direct global -> LDS DMA, no registers).
+//
+// A 128 x 128 bf16 tile occupies 32 KiB of LDS: row r (token key0 + r) at
+// byte r*256, its sixteen 16-byte chunks permuted by an XOR swizzle so that
+// the reads the MFMA operands need hit distinct LDS banks:
+//   K tiles: physical chunk = logical chunk ^ (r % 16)   (row-wise ds_read_b128)
+//   V tiles: physical chunk = logical chunk ^ 4*(r % 4)  (ds_read_b64_tr_b16)
+// One global_load_lds_dwordx4 moves 64 lanes x 16 B into 1 KiB of LDS (lane i
+// to byte 16*i), i.e. four rows. Rows at or past n_tokens load row
+// n_tokens-1 instead; such keys are masked out of the softmax and get zero
+// weight, so their values never matter.
+
+constexpr int kTileBytes = kBlock * kDim * 2;   // 32 KiB
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void global_cvoid;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+template <int kSwizzleV>
+__device__ __forceinline__ void dma_tile(uint8_t* lds_tile, const uint16_t* __restrict__ src,
+                                         int64_t stride_token, int key0, int n_tokens,
+                                         int first_chunk, int n_chunks, int lane) {
+  const int sub = lane >> 4, p = lane & 15;
+  for (int j = 0; j < n_chunks; ++j) {
+    const int I = first_chunk + j;              // 1 KiB chunk = rows 4I .. 4I+3
+    const int row = 4 * I + sub;
+    const int c = kSwizzleV ? (p ^ ((row & 3) << 2)) : (p ^ (row & 15));
+    const int tok = key0 + row < n_tokens ? key0 + row : n_tokens - 1;
+    const uint16_t* gp = src + (int64_t)tok * stride_token + c * 8;
+    __builtin_amdgcn_global_load_lds((global_cvoid*)gp, (lds_void*)(lds_tile + I * 1024), 16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// LDS byte offset of the K operand for d-step s (0..7) of a lane whose
+// A-operand row is `row` (r % 16 == row % 16) and lane group g.
+__device__ __forceinline__ int k_operand_offset(int row, int s, int g) {
+  return row * 256 + ((((2 * s + g) ^ (row & 15))) << 4);
+}
+
+// Transposed read of V for the P.V product. For 16-key group s of the tile
+// and output tile u (d = 32u .. 32u+31), the A operand of lane l holds
+// V[key][32u + l%32] for the eight keys 16s + 4g + {0..3} and
+// 16s + 8 + 4g + {0..3} (g = l/32). ds_read_b64_tr_b16 hands lane i of each
+// 16-lane group element i%4 of the 8 bytes read by lanes 4m + i/4, m = 0..3,
+// so lane (m = (l%16)/4, q = l%4) of group j = l/16 reads the four d values
+// 32u + 16(j%2) + 4q .. +3 of key 16s + 8h + 4(j/2) + m (h = 0, then 1).
+// v_operand_offset gives the swizzled byte offset for s = 0, h = 0; key
+// group s adds s*4096 and h = 1 adds 2048.
+__device__ __forceinline__ int v_operand_offset(int u, int lane) {
+  const int j = lane >> 4, m = (lane >> 2) & 3, q = lane & 3;
+  const int row = 4 * (j >> 1) + m;
+  const int chunk = (4 * u + 2 * (j & 1) + (q >> 1)) ^ (4 * m);
+  return row * 256 + chunk * 16 + (q & 1) * 8;
+}
+
+__device__ __forceinline__ bf16x8 v_operand(const uint8_t* vtile, int off) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(vtile + off));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(vtile + off + 2048));
+  const bf16x4 a = __builtin_bit_cast(bf16x4, lo), b = __builtin_bit_cast(bf16x4, hi);
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 }  // namespace calibatt
