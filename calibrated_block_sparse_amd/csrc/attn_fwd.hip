@@ -10,22 +10,50 @@
 //
 // One workgroup = one 128-query tile of one head (a query block of a
 // non-repeat head, or 128 consecutive anchor queries of a repeat head).
-// Per kept key block: stage K (row-major) and V (transposed) in LDS,
-// S^T = K Q^T on bf16 MFMA, online softmax in fp32 with exp2, O^T += V^T P^T
-// on bf16 MFMA. Two workgroups share a CU so that one's softmax and tile
-// loads overlap the other's MFMA work.
+// Per kept key block:
+//   S^T = K Q^T on bf16 MFMA (Q held in registers for the whole tile),
+//   online softmax in fp32 with exp2,
+//   O^T += V^T P^T on bf16 MFMA (P stays in registers).
+// K and V tiles are copied global -> LDS by the load unit directly (no
+// register round trip). The copy of K for the next kept block starts as
+// soon as every wave has finished reading the current K tile and runs under
+// the softmax and the P.V product; the copy of V for the next block runs
+// under the next S^T product. 64 KiB of LDS per workgroup, two workgroups per
+// CU, so one workgroup's softmax overlaps the other's MFMA work.
 #include "device_common.h"
 #include "kernels.h"
 
 namespace calibatt {
 
+// The running row max is only raised when a block's max exceeds it by more
+// than this many powers of two. Probabilities computed against a stale max
+// are at most 2^8 and the final division by the row sum cancels the choice
+// of reference exactly, so this saves the rescale of the output accumulator
+// on almost every block without changing the result.
+constexpr float kLazyRescaleLog2 = 8.f;
+
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sK[kBlock * kLdsStride];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[kDim * kLdsStride];
+  // Dynamic LDS (2 tiles): its contents are written by the copy engine
+  // behind the compiler's back, so it must not be a static object the
+  // compiler believes it fully sees.
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+  uint8_t* const sK = smem;
+  uint8_t* const sV = smem + kTileBytes;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
+  const uint32_t ldsK = lds_addr(sK), ldsV = lds_addr(sV);
 
   // ---- which tile
   const int item = xcd_remap(blockIdx.x, a.n_items);
@@ -70,8 +98,13 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const AttnArgs a)
   }
   bf16x8 qf[8];
   load_query(qf, qh, st, qtok, qvalid, g);
+  // Make the compiler wait for the query loads here, before any tile copy
+  // is in flight (it does not see the copies and would otherwise wait for
+  // everything outstanding at the first use inside the loop).
+#pragma unroll
+  for (int s = 0; s < 8; ++s) asm volatile("" ::"v"(qf[s]));
 
-  // ---- kept-block range
+  // ---- kept-block range [beg, end): list positions (sparse) or blocks (repeat)
   int beg = 0, end = R;
   if (!rep) {
     const int64_t row = (int64_t)head * R + tile;
@@ -81,7 +114,15 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const AttnArgs a)
     beg = (int)b;
     end = (int)e;
   }
+  // Key block at list position `it`; an index outside [0, R) is loaded as
+  // block 0 and contributes nothing (all of its keys are masked). The list
+  // is read-only for the kernel's lifetime, so it is read with scalar loads
+  // (constant address space), which the tile copies do not wait behind.
+  const __attribute__((address_space(4))) int32_t* idx4 =
+      (const __attribute__((address_space(4))) int32_t*)a.indices;
+  auto block_at = [&](int it) -> int { return rep ? it : idx4[it]; };
 
+  const CopyPlan cp = make_copy_plan(st, lane);
   const float sl = a.scale_log2;
   float m_run = -__builtin_inff();
   float l_run = 0.f;
@@ -89,56 +130,111 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const AttnArgs a)
 #pragma unroll
   for (int u = 0; u < 4; ++u) oacc[u] = f32x16{};
 
-  for (int it = beg; it < end; ++it) {
-    const int c = rep ? it : __builtin_amdgcn_readfirstlane(a.indices[it]);
-    if ((unsigned)c >= (unsigned)R) continue;
-    const int key0 = c * kBlock;
+  int c = 0;
+  if (beg < end) {
+    c = block_at(beg);
+    const int cl = (unsigned)c < (unsigned)R ? c : 0;
+    copy_tile<false>(ldsK, kh, cp, cl * kBlock, N, wave, lane);
+    copy_tile<true>(ldsV, vh, cp, cl * kBlock, N, wave, lane);
+  }
 
-    __syncthreads();  // previous block's LDS reads are done
-    stage_rows(sK, kh, st, key0, N, tid);
-    stage_values_transposed(sV, vh, st, key0, N, tid);
-    __syncthreads();
+  for (int it = beg; it < end; ++it) {
+    const bool has_next = it + 1 < end;
+    const int cn = has_next ? block_at(it + 1) : 0;
+    const int cnl = (unsigned)cn < (unsigned)R ? cn : 0;
+    const int key0 = c * kBlock;
+    // valid keys of this block: 0 for an out-of-range index
+    const int key_lim = (unsigned)c < (unsigned)R ? (N - key0 < kBlock ? N - key0 : kBlock) : 0;
+
+    // ---- K(it) is in LDS once this lane's copies of it have landed and
+    // every wave has passed the barrier (V(it) may still be in flight).
+    wait_vmem<kCopiesPerTile>();
+    lds_barrier();
 
     f32x16 sacc[4];
-    scores_transposed(sacc, sK, qf, l32, g);
-    mask_ragged_keys(sacc, key0, N, g);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) sacc[t] = f32x16{};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        // row 32t + l32 has the same swizzle as row l32
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sK + 32 * t * 256 + k_operand_offset(l32, s, g));
+        sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[t], 0, 0, 0);
+      }
+    }
+    lds_barrier();  // every wave is done with sK
+    if (has_next) copy_tile<false>(ldsK, kh, cp, cnl * kBlock, N, wave, lane);
 
+    if (key_lim < kBlock) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (acc_key(t, i, g) >= key_lim) sacc[t][i] = -__builtin_inff();
+    }
+
+    // ---- online softmax (log2 units)
     float mx = -__builtin_inff();
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(mx, sacc[t][i]);
-    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = __builtin_fmaxf(m_run, mx * sl);
-    const float alpha = (m_run == -__builtin_inff()) ? 0.f : fast_exp2(m_run - m_new);
-    m_run = m_new;
+    mx = pair_max(mx);
+    const float mblk = mx * sl;
+    const bool up = mblk > m_run + kLazyRescaleLog2;
+    if (__builtin_amdgcn_ballot_w64(up)) {
+      const float m_new = up ? mblk : m_run;
+      const float alpha = m_new == m_run ? 1.f : fast_exp2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) oacc[u] *= alpha;
+      m_run = m_new;
+    }
+    const float mref = m_run == -__builtin_inff() ? 0.f : m_run;
 
-    float lsum = 0.f;
     bf16x8 pf[8];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = fast_exp2(__builtin_fmaf(sacc[t][i], sl, -m_new));
-        lsum += p;
-        pf[2 * t + (i >> 3)][i & 7] = (__bf16)p;
-      }
-    l_run = l_run * alpha + lsum;
+      for (int i = 0; i < 16; ++i)
+        pf[2 * t + (i >> 3)][i & 7] = (__bf16)fast_exp2(__builtin_fmaf(sacc[t][i], sl, -mref));
+    // The row sum adds the same bf16-rounded probabilities that enter P.V,
+    // so a dominant key's rounding cancels between numerator and denominator
+    // (it would not with a stale reference max). Two per dot instruction.
+    {
+      const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+      float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) oacc[u] *= alpha;
+      for (int s = 0; s < 8; ++s) {
+        ls0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[s], pf[s], 0, 1), ones, ls0, false);
+        ls1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[s], pf[s], 2, 3), ones, ls1, false);
+        ls0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[s], pf[s], 4, 5), ones, ls0, false);
+        ls1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[s], pf[s], 6, 7), ones, ls1, false);
+      }
+      l_run += ls0 + ls1;
+    }
+
+    // ---- V(it) in LDS (K(it+1) may still be in flight)
+    if (has_next) wait_vmem<kCopiesPerTile>();
+    else wait_vmem<0>();
+    lds_barrier();
 
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(sV + (32 * u + l32) * kLdsStride + 16 * s + 8 * g);
+        const bf16x8 vf = v_operand(sV + s * 4096, v_operand_offset(u, lane));
         oacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[s], oacc[u], 0, 0, 0);
       }
     }
+    lds_barrier();  // every wave is done with sV
+    if (has_next) copy_tile<true>(ldsV, vh, cp, cnl * kBlock, N, wave, lane);
+    c = cn;
   }
 
   // ---- epilogue: normalise and store (broadcast for repeat heads)
-  const float ltot = l_run + __shfl_xor(l_run, 32);
+  const float ltot = pair_sum(l_run);
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
   if (!qvalid) return;
   u32x2 packed[4][4];
@@ -171,7 +267,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const AttnArgs a)
 
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream) {
   if (a.n_items <= 0) return hipSuccess;
-  hipLaunchKernelGGL(attn_fwd_kernel, dim3(a.n_items), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL(attn_fwd_kernel, dim3(a.n_items), dim3(kThreads), 2 * kTileBytes, stream, a);
   return hipGetLastError();
 }
 

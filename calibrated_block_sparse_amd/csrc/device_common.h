@@ -28,6 +28,7 @@ constexpr int kThreads = 256;     // 4 waves
 constexpr int kLdsStride = 136;   // bf16 per LDS tile row: 256 B + 16 B pad
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -156,41 +157,116 @@ __device__ __forceinline__ void mask_ragged_keys(f32x16 (&sacc)[4], int key0, in
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---------------------------------------------------------------------------
-// Asynchronous tile staging (direct global -> LDS DMA, no registers).
+// Asynchronous tile staging (direct global -> LDS copies, no registers).
 //
 // A 128 x 128 bf16 tile occupies 32 KiB of LDS: row r (token key0 + r) at
 // byte r*256, its sixteen 16-byte chunks permuted by an XOR swizzle so that
 // the reads the MFMA operands need hit distinct LDS banks:
 //   K tiles: physical chunk = logical chunk ^ (r % 16)   (row-wise ds_read_b128)
 //   V tiles: physical chunk = logical chunk ^ 4*(r % 4)  (ds_read_b64_tr_b16)
-// One global_load_lds_dwordx4 moves 64 lanes x 16 B into 1 KiB of LDS (lane i
-// to byte 16*i), i.e. four rows. Rows at or past n_tokens load row
-// n_tokens-1 instead; such keys are masked out of the softmax and get zero
-// weight, so their values never matter.
+// One global_load_lds_dwordx4 moves 64 lanes x 16 B into 1 KiB of LDS (lane
+// i to byte 16*i of the block M0 points at), i.e. four rows. Wave w copies
+// rows 32w .. 32w+31 with eight such instructions; instruction j covers rows
+// 32w + 4j + (lane / 16), lane % 16 being the physical chunk.
+//
+// The copies are issued from inline assembly on purpose: the compiler
+// cannot tell which LDS buffer a copy writes and would otherwise wait for
+// every copy in flight before any LDS read or barrier, which serialises the
+// prefetch. Completion is tracked by hand with s_waitcnt vmcnt (copies
+// retire in issue order) followed by a workgroup barrier. Setting M0 needs
+// one wait state before the copy that reads it.
 
 constexpr int kTileBytes = kBlock * kDim * 2;   // 32 KiB
+constexpr int kCopiesPerTile = 8;               // per wave
 
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) const void global_cvoid;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
-template <int kSwizzleV>
-__device__ __forceinline__ void dma_tile(uint8_t* lds_tile, const uint16_t* __restrict__ src,
-                                         int64_t stride_token, int key0, int n_tokens,
-                                         int first_chunk, int n_chunks, int lane) {
-  const int sub = lane >> 4, p = lane & 15;
-  for (int j = 0; j < n_chunks; ++j) {
-    const int I = first_chunk + j;              // 1 KiB chunk = rows 4I .. 4I+3
-    const int row = 4 * I + sub;
-    const int c = kSwizzleV ? (p ^ ((row & 3) << 2)) : (p ^ (row & 15));
-    const int tok = key0 + row < n_tokens ? key0 + row : n_tokens - 1;
-    const uint16_t* gp = src + (int64_t)tok * stride_token + c * 8;
-    __builtin_amdgcn_global_load_lds((global_cvoid*)gp, (lds_void*)(lds_tile + I * 1024), 16, 0, 0);
-  }
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// 16 bytes per lane from sbase + voff into LDS [lds + 16*lane]. sbase and lds
+// must be wave-uniform.
+__device__ __forceinline__ void copy16_saddr(uint32_t lds, const void* sbase, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(lds), "v"(voff), "s"(sbase) : "memory", "m0");
+}
+
+// Same with a per-lane 64-bit address.
+__device__ __forceinline__ void copy16_vaddr(uint32_t lds, const void* vaddr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(lds), "v"(vaddr) : "memory", "m0");
+}
+
+#pragma clang diagnostic pop
+
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier without a memory fence: this wave's LDS reads have
+// returned, then every wave of the workgroup arrives. (A __syncthreads fence
+// would also wait for all copies in flight.)
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Per-lane source offsets of the fast (unclamped) copy path, fixed for the
+// kernel: K needs one per j % 4 (its swizzle repeats every 16 rows), V one.
+struct CopyPlan {
+  uint32_t k_off[4];
+  uint32_t v_off;
+  int64_t row_bytes;   // stride_token * 2
+};
+
+__device__ __forceinline__ CopyPlan make_copy_plan(int64_t stride_token, int lane) {
+  CopyPlan cp;
+  const int sub = lane >> 4, p = lane & 15;
+  cp.row_bytes = stride_token * 2;
+#pragma unroll
+  for (int jm = 0; jm < 4; ++jm) {
+    const int r = 4 * jm + sub;  // row modulo 16
+    cp.k_off[jm] = (uint32_t)(r * cp.row_bytes + ((p ^ r) << 4));
+  }
+  cp.v_off = (uint32_t)(sub * cp.row_bytes + ((p ^ (sub << 2)) << 4));
+  return cp;
+}
+
+// Issues this wave's eight copies of the tile whose first token row is key0
+// (kIsV selects the V swizzle). Rows at or past n_tokens are read from row
+// n_tokens - 1 instead (their keys are masked out of the softmax, so those
+// values never matter).
+template <bool kIsV>
+__device__ __forceinline__ void copy_tile(uint32_t lds_tile, const uint16_t* __restrict__ src,
+                                          const CopyPlan& cp, int key0, int n_tokens, int wave,
+                                          int lane) {
+  const uint32_t lds = lds_tile + wave * (kCopiesPerTile * 1024);
+  if (key0 + kBlock <= n_tokens) {
+    const char* base = reinterpret_cast<const char*>(src) + (int64_t)(key0 + 32 * wave) * cp.row_bytes;
+#pragma unroll
+    for (int j = 0; j < kCopiesPerTile; ++j) {
+      if (kIsV)
+        copy16_saddr(lds + 1024 * j, base + (int64_t)(4 * j) * cp.row_bytes, cp.v_off);
+      else
+        copy16_saddr(lds + 1024 * j, base + (int64_t)(16 * (j >> 2)) * cp.row_bytes, cp.k_off[j & 3]);
+    }
+  } else {
+    const int sub = lane >> 4, p = lane & 15;
+#pragma unroll
+    for (int j = 0; j < kCopiesPerTile; ++j) {
+      const int row = 32 * wave + 4 * j + sub;
+      const int chunk = kIsV ? (p ^ ((row & 3) << 2)) : (p ^ (row & 15));
+      const int tok = key0 + row < n_tokens ? key0 + row : n_tokens - 1;
+      copy16_vaddr(lds + 1024 * j, reinterpret_cast<const char*>(src) + (int64_t)tok * cp.row_bytes + chunk * 16);
+    }
+  }
+}
 
 // LDS byte offset of the K operand for d-step s (0..7) of a lane whose
 // A-operand row is `row` (r % 16 == row % 16) and lane group g.
