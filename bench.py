@@ -37,7 +37,8 @@ HBM_PEAK_GBS = 8000.0
 PAIR_FLOP = 4.0 * 128 * 128 * 128  # QK^T and PV of one 128x128 block, D = 128
 METRIC = "effective TFLOP/s on kept blocks + speedup vs dense mask, Wan-720p shape, 1 GPU"
 KERNEL_SOURCES = ("calibrated_block_sparse_amd/csrc/attn_fwd.hip",
-                  "calibrated_block_sparse_amd/csrc/device_common.h")
+                  "calibrated_block_sparse_amd/csrc/device_common.h",
+                  "calibrated_block_sparse_amd/build.py")
 
 
 def log(*a):
@@ -90,8 +91,11 @@ def attn_case(cbs, name: str, steps: int, warmup: int, dense: bool = False):
     pairs = int(idx.numel()) if flags is None else int(
         mask[flags == 0].sum() + int(flags.sum()) * -(-(w.grid.frames * w.anchors * w.grid.cols) // 128) * w.n_blocks)
 
+    ws = torch.empty(cbs.calibatt_sparse_attn_fwd_workspace(w.heads, w.n_tokens), dtype=torch.uint8,
+                     device="cuda")
+
     def step():
-        cbs.calibatt_sparse_attn_fwd(q, k, v, o, off, idx, w.scale, flags, grid)
+        cbs.calibatt_sparse_attn_fwd(q, k, v, o, off, idx, w.scale, flags, grid, workspace=ws)
 
     per, total = time_launches(step, steps, warmup)
     return dict(workload=w, pairs=pairs, per_ms=per, total_ms=total, mask=mask, tensors=(q, k, v))

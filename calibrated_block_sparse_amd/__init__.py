@@ -32,7 +32,8 @@ SIGNATURES = {
     "calibatt_abi_version": (_c.c_int32, []),
     "calibatt_sparse_attn_fwd": (_c.c_int, [_p, _p, _p, _p, _c.c_int32, _c.c_int32, _c.c_int32,
                                             _c.c_int64, _c.c_int64, _c.c_float, _p, _p,
-                                            _c.c_int64, _p, _p, _p]),
+                                            _c.c_int64, _p, _p, _p, _c.c_size_t, _p]),
+    "calibatt_sparse_attn_fwd_workspace": (_c.c_size_t, [_c.c_int32, _c.c_int32]),
     "calibatt_block_energy_workspace": (_c.c_size_t, [_c.c_int32, _c.c_int32]),
     "calibatt_block_energy": (_c.c_int, [_p, _p, _p, _c.c_int32, _c.c_int32, _c.c_int32,
                                          _c.c_int64, _c.c_int64, _c.c_float, _p, _c.c_size_t, _p]),
@@ -124,12 +125,18 @@ def calibatt_abi_version() -> int:
     return int(load_library().calibatt_abi_version())
 
 
+def calibatt_sparse_attn_fwd_workspace(heads: int, n_tokens: int) -> int:
+    return int(load_library().calibatt_sparse_attn_fwd_workspace(heads, n_tokens))
+
+
 def calibatt_sparse_attn_fwd(q, k, v, o, kv_offsets, kv_indices, scale: float,
-                             repeat_flags=None, grid=None, stream=None) -> None:
+                             repeat_flags=None, grid=None, stream=None, workspace=None) -> None:
     """o <- block-sparse attention of q, k, v over the kept-block lists
     (kv_offsets int32 [H*R+1], kv_indices int32 [nnz], CUDA tensors).
     repeat_flags: host sequence of H ints (or None); grid: (frames, rows,
-    cols, anchors) for repeat heads."""
+    cols, anchors) for repeat heads. workspace: uint8 CUDA tensor of
+    calibatt_sparse_attn_fwd_workspace bytes (allocated here through torch
+    when None)."""
     H, N, D, sh, stok = _attn_layout("calibatt_sparse_attn_fwd", q, k, v, o)
     for t in (kv_offsets, kv_indices):
         if t is not None and (t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous()):
@@ -145,9 +152,14 @@ def calibatt_sparse_attn_fwd(q, k, v, o, kv_offsets, kv_indices, scale: float,
     if grid is not None:
         g = ctypes.byref(Grid(*[int(x) for x in grid]))
     lib = load_library()
+    if workspace is None:
+        need = calibatt_sparse_attn_fwd_workspace(H, N)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     rc = lib.calibatt_sparse_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), H, N, D, sh, stok,
                                       float(scale), _ptr(kv_offsets), _ptr(kv_indices), nnz,
-                                      flags, g, _stream(stream))
+                                      flags, g, _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(),
+                                      _stream(stream))
     _check("calibatt_sparse_attn_fwd", rc)
 
 

@@ -26,6 +26,9 @@ HIP_FLAGS = [
     "-Wall", "-Wno-unused-function",
     # keep the compiler from forming packed fp32 arithmetic
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in ordinary VGPRs: the scores feed VALU softmax code, and
+    # the accumulation-register form costs a copy per value
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"),
 ]
 

@@ -14,14 +14,27 @@
 //   S^T = K Q^T on bf16 MFMA (Q held in registers for the whole tile),
 //   online softmax in fp32 with exp2,
 //   O^T += V^T P^T on bf16 MFMA (P stays in registers).
-// K and V tiles are copied global -> LDS by the load unit directly (no
-// register round trip). The copy of K for the next kept block starts as
-// soon as every wave has finished reading the current K tile and runs under
-// the softmax and the P.V product; the copy of V for the next block runs
-// under the next S^T product. 64 KiB of LDS per workgroup, two workgroups per
-// CU, so one workgroup's softmax overlaps the other's MFMA work.
+// K tiles and transposed V tiles are copied global -> LDS by the load unit
+// directly (no register round trip). The copy of K for the next kept block
+// starts as soon as every wave has finished reading the current K tile and
+// runs under the softmax and the P.V product; the copy of V for the next
+// block runs under the next S^T product. 64 KiB of LDS per workgroup, two
+// workgroups per CU, so one workgroup's softmax overlaps the other's MFMA
+// work.
+//
+// V is used transposed. The P.V product needs, per lane, eight keys of one
+// head-dimension column; reading them out of key-major V in LDS takes
+// transposing 8-byte reads, which move half the bytes per LDS cycle of a
+// 16-byte read and made LDS bandwidth the bound of the whole kernel. So a
+// pre-pass (v_transpose_kernel, HBM-bound, about 1% of the attention time)
+// writes every 128-key block of V as a [128 d][128 keys] tile into the
+// caller's workspace, keys permuted inside each group of 16 as
+// 0-3, 8-11, 4-7, 12-15 -- the order in which a lane holds its
+// probabilities. V^T tiles then go through exactly the K-tile path: same
+// copy, same swizzle, same 16-byte operand reads.
 #include "device_common.h"
 #include "kernels.h"
+
 
 namespace calibatt {
 
@@ -32,6 +45,11 @@ namespace calibatt {
 // on almost every block without changing the result.
 constexpr float kLazyRescaleLog2 = 8.f;
 
+// LDS operand reads kept in flight ahead of the MFMA that uses them.
+#ifndef CALIBATT_READ_DEPTH
+#define CALIBATT_READ_DEPTH 3
+#endif
+
 __device__ __forceinline__ float pair_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -40,6 +58,22 @@ __device__ __forceinline__ float pair_max(float x) {
 __device__ __forceinline__ float pair_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Instruction order inside a scheduling region of kM MFMAs that each take
+// one LDS operand read: kDepth reads up front, then per MFMA the read kDepth
+// ahead and kV vector instructions. Left to itself the compiler issues each
+// read right before its MFMA and waits for it, exposing the LDS latency on
+// every MFMA.
+template <int kM, int kDepth, int kV>
+__device__ __forceinline__ void pipeline_reads() {
+  __builtin_amdgcn_sched_group_barrier(0x100, kDepth, 0);  // DS reads
+#pragma unroll
+  for (int i = 0; i < kM; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
+    if (i + kDepth < kM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (kV > 0) __builtin_amdgcn_sched_group_barrier(0x002, kV, 0);  // VALU
+  }
 }
 
 __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const AttnArgs a) {
@@ -123,6 +157,14 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const AttnArgs a)
   auto block_at = [&](int it) -> int { return rep ? it : idx4[it]; };
 
   const CopyPlan cp = make_copy_plan(st, lane);
+  const CopyPlan cpt = make_copy_plan(kBlock, lane);   // V^T tiles: 256-byte rows
+  const uint16_t* __restrict__ vth = a.vt + (int64_t)head * R * (kBlock * kDim);
+  // Per-lane LDS base address of the K operand for d-step s; K rows 32t + l32
+  // and V^T rows 32u + l32 share the swizzle of row l32, so the tile, the
+  // sub-tile and the K/V choice are compile-time displacements.
+  uint32_t kaddr[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) kaddr[s] = ldsK + (uint32_t)k_operand_offset(l32, s, g);
   const float sl = a.scale_log2;
   float m_run = -__builtin_inff();
   float l_run = 0.f;
@@ -135,8 +177,136 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const AttnArgs a)
     c = block_at(beg);
     const int cl = (unsigned)c < (unsigned)R ? c : 0;
     copy_tile<false>(ldsK, kh, cp, cl * kBlock, N, wave, lane);
-    copy_tile<true>(ldsV, vh, cp, cl * kBlock, N, wave, lane);
+    copy_tile<false>(ldsV, vth, cpt, cl * kBlock, R * kBlock, wave, lane);
   }
+
+  // S^T tile t (keys 32t .. 32t+31 of the block x this wave's 32 queries).
+  auto qk_tile = [&](f32x16& sa, int t) {
+    sa = f32x16{};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const bf16x8 kf = lds_read_b128(kaddr[s] + 8192 * t);
+      sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sa, 0, 0, 0);
+    }
+  };
+
+  // Probabilities of score tile t against the reference `mref` (16 per
+  // lane, as bf16), and the tile's running max into `mx`. Keys past the end
+  // of a ragged block were loaded as copies of key N-1, so their scores
+  // repeat a real score of the same block and leave the max unchanged;
+  // their probabilities are zeroed afterwards (zero_masked_probs).
+  auto probs_tile = [&](f32x16& sa, bf16x8& p_lo, bf16x8& p_hi, float mref, float& mx) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      p_lo[i] = (__bf16)fast_exp2(__builtin_fmaf(sa[i], sl, -mref));
+      p_hi[i] = (__bf16)fast_exp2(__builtin_fmaf(sa[8 + i], sl, -mref));
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(mx, sa[i]);
+    // Keep these exponentials next to the next tile's MFMAs: without this
+    // use the compiler sinks them past the rescale test (whose rare path
+    // recomputes them), where no MFMA is left to overlap them.
+    asm volatile("" ::"v"(p_lo), "v"(p_hi));
+  };
+
+  // O^T += V^T P^T for key groups s0 .. s0+3 (16 keys each). The A operand
+  // of lane (l32, g) for output tile u and key group s is V^T row 32u + l32,
+  // logical chunk 2s + g: the K-operand address of d-step s, moved to the
+  // V^T tile.
+  auto pv_steps = [&](const bf16x8 (&pf)[8], int s0) {
+#pragma unroll
+    for (int s = s0; s < s0 + 4; ++s) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bf16x8 vf = lds_read_b128(kaddr[s] + kTileBytes + 8192 * u);
+        oacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[s], oacc[u], 0, 0, 0);
+      }
+    }
+  };
+
+  // Row sum of the bf16-rounded probabilities that enter P.V, so a dominant
+  // key's rounding cancels between numerator and denominator (it would not
+  // with a stale reference max). Two per dot instruction.
+  auto add_row_sum = [&](const bf16x8 (&pf)[8]) {
+    const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+    float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      ls0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[s], pf[s], 0, 1), ones, ls0, false);
+      ls1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[s], pf[s], 2, 3), ones, ls1, false);
+      ls0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[s], pf[s], 4, 5), ones, ls0, false);
+      ls1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[s], pf[s], 6, 7), ones, ls1, false);
+    }
+    l_run += ls0 + ls1;
+  };
+
+  // Zeroes the probabilities of keys at or past key_lim (ragged last block;
+  // every key of an out-of-range index). Dword d of pf[s] holds the bf16
+  // pair of keys 16s + 8(d/2) + 4g + 2(d%2) + {0, 1}; the mask is built with
+  // integer arithmetic (no per-element compares held in scalar registers).
+  auto zero_masked_probs = [&](bf16x8 (&pf)[8], int key_lim) {
+    const int t0 = key_lim - 4 * g;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      u32x4 w = __builtin_bit_cast(u32x4, pf[s]);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        int n = t0 - (16 * s + 8 * (d >> 1) + 2 * (d & 1));  // valid keys in the pair
+        n = n < 0 ? 0 : (n > 2 ? 2 : n);
+        const uint32_t mask = (uint32_t)(n > 0 ? 1 : 0) * 0xffffu | (uint32_t)(n >> 1) * 0xffff0000u;
+        w[d] &= mask;
+      }
+      pf[s] = __builtin_bit_cast(bf16x8, w);
+    }
+  };
+
+  // Scores and probabilities of one block. The probabilities are computed
+  // against the current reference max before this block's max is known, so
+  // the exponentials of tile t overlap the MFMAs of tile t+1. The running
+  // max is only raised when the block's max exceeds it by more than
+  // 2^kLazyRescaleLog2 (first block, rarely later); then the output is
+  // rescaled and the block recomputed from the K tile still in LDS.
+  auto scores_probs = [&](bf16x8 (&pf)[8]) {
+    const float mref = m_run == -__builtin_inff() ? 0.f : m_run;
+    float mx = -__builtin_inff();
+    f32x16 sa, sb;
+    // Scheduling fences keep each stage's operand loads next to its MFMAs
+    // (hoisting all of them would exceed the register budget).
+    qk_tile(sa, 0);
+    pipeline_reads<8, CALIBATT_READ_DEPTH, 0>();
+    __builtin_amdgcn_sched_barrier(0);
+    qk_tile(sb, 1);
+    probs_tile(sa, pf[0], pf[1], mref, mx);
+    pipeline_reads<8, CALIBATT_READ_DEPTH, 6>();
+    __builtin_amdgcn_sched_barrier(0);
+    qk_tile(sa, 2);
+    probs_tile(sb, pf[2], pf[3], mref, mx);
+    pipeline_reads<8, CALIBATT_READ_DEPTH, 6>();
+    __builtin_amdgcn_sched_barrier(0);
+    qk_tile(sb, 3);
+    probs_tile(sa, pf[4], pf[5], mref, mx);
+    pipeline_reads<8, CALIBATT_READ_DEPTH, 6>();
+    __builtin_amdgcn_sched_barrier(0);
+    probs_tile(sb, pf[6], pf[7], mref, mx);
+    const float mblk = pair_max(mx) * sl;
+    const bool up = mblk > m_run + kLazyRescaleLog2;
+    if (__builtin_amdgcn_ballot_w64(up)) {
+      const float m_new = up ? mblk : m_run;
+      const float alpha = m_new == m_run ? 1.f : fast_exp2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) oacc[u] *= alpha;
+      m_run = m_new;
+      const float mref2 = m_run == -__builtin_inff() ? 0.f : m_run;
+      float unused = 0.f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        qk_tile(sa, t);
+        probs_tile(sa, pf[2 * t], pf[2 * t + 1], mref2, unused);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
 
   for (int it = beg; it < end; ++it) {
     const bool has_next = it + 1 < end;
@@ -151,85 +321,24 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const AttnArgs a)
     wait_vmem<kCopiesPerTile>();
     lds_barrier();
 
-    f32x16 sacc[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) sacc[t] = f32x16{};
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        // row 32t + l32 has the same swizzle as row l32
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sK + 32 * t * 256 + k_operand_offset(l32, s, g));
-        sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[t], 0, 0, 0);
-      }
-    }
+    bf16x8 pf[8];
+    scores_probs(pf);
+    if (key_lim < kBlock) zero_masked_probs(pf, key_lim);
     lds_barrier();  // every wave is done with sK
     if (has_next) copy_tile<false>(ldsK, kh, cp, cnl * kBlock, N, wave, lane);
-
-    if (key_lim < kBlock) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (acc_key(t, i, g) >= key_lim) sacc[t][i] = -__builtin_inff();
-    }
-
-    // ---- online softmax (log2 units)
-    float mx = -__builtin_inff();
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(mx, sacc[t][i]);
-    mx = pair_max(mx);
-    const float mblk = mx * sl;
-    const bool up = mblk > m_run + kLazyRescaleLog2;
-    if (__builtin_amdgcn_ballot_w64(up)) {
-      const float m_new = up ? mblk : m_run;
-      const float alpha = m_new == m_run ? 1.f : fast_exp2(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) oacc[u] *= alpha;
-      m_run = m_new;
-    }
-    const float mref = m_run == -__builtin_inff() ? 0.f : m_run;
-
-    bf16x8 pf[8];
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        pf[2 * t + (i >> 3)][i & 7] = (__bf16)fast_exp2(__builtin_fmaf(sacc[t][i], sl, -mref));
-    // The row sum adds the same bf16-rounded probabilities that enter P.V,
-    // so a dominant key's rounding cancels between numerator and denominator
-    // (it would not with a stale reference max). Two per dot instruction.
-    {
-      const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
-      float ls0 = 0.f, ls1 = 0.f;
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        ls0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[s], pf[s], 0, 1), ones, ls0, false);
-        ls1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[s], pf[s], 2, 3), ones, ls1, false);
-        ls0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[s], pf[s], 4, 5), ones, ls0, false);
-        ls1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[s], pf[s], 6, 7), ones, ls1, false);
-      }
-      l_run += ls0 + ls1;
-    }
 
     // ---- V(it) in LDS (K(it+1) may still be in flight)
     if (has_next) wait_vmem<kCopiesPerTile>();
     else wait_vmem<0>();
     lds_barrier();
-
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const bf16x8 vf = v_operand(sV + s * 4096, v_operand_offset(u, lane));
-        oacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[s], oacc[u], 0, 0, 0);
-      }
-    }
+    pv_steps(pf, 0);
+    add_row_sum(pf);
+    pipeline_reads<16, CALIBATT_READ_DEPTH, 2>();
+    __builtin_amdgcn_sched_barrier(0);
+    pv_steps(pf, 4);
+    pipeline_reads<16, CALIBATT_READ_DEPTH, 0>();
     lds_barrier();  // every wave is done with sV
-    if (has_next) copy_tile<true>(ldsV, vh, cp, cnl * kBlock, N, wave, lane);
+    if (has_next) copy_tile<false>(ldsV, vth, cpt, cnl * kBlock, R * kBlock, wave, lane);
     c = cn;
   }
 
@@ -263,6 +372,58 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const AttnArgs a)
       for (int b = 0; b < 4; ++b)
         *reinterpret_cast<u32x2*>(dst + 32 * u + 8 * b + 4 * g) = packed[u][b];
   }
+}
+
+// V^T pre-pass: one workgroup per (head, 128-key block). Reads the block's
+// rows of V (rows at or past N read as zero), writes the [128 d][128 keys]
+// tile with keys permuted inside each group of 16 as 0-3, 8-11, 4-7, 12-15.
+// Staged through LDS with rows padded by 4 bytes, so the column reads of
+// eight different keys fall in different banks.
+__global__ void __launch_bounds__(kThreads) v_transpose_kernel(const VtArgs a) {
+  constexpr int kPitch = kDim * 2 + 4;  // bytes per staged key row
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kBlock * kPitch];
+  const int tid = threadIdx.x;
+  const int head = blockIdx.x / a.n_blocks, c = blockIdx.x % a.n_blocks;
+  const uint16_t* __restrict__ src = a.v + (int64_t)head * a.stride_head;
+  // load: 128 rows x 16 chunks of 16 bytes
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int idx = tid + kThreads * j;
+    const int row = idx >> 4, ch = idx & 15;
+    const int tok = c * kBlock + row;
+    const u32x4 w = tok < a.n_tokens ? load16(src + (int64_t)tok * a.stride_token + ch * 8)
+                                     : u32x4{0u, 0u, 0u, 0u};
+    uint32_t* d = reinterpret_cast<uint32_t*>(tile + row * kPitch + ch * 16);
+    d[0] = w[0]; d[1] = w[1]; d[2] = w[2]; d[3] = w[3];
+  }
+  __syncthreads();
+  // store: task = (pair of d columns, 8-key chunk); chunk cc covers keys
+  // 16(cc/2) + 8(e/4) + 4(cc%2) + e%4, e = 0..7
+  uint16_t* __restrict__ dst = a.vt + ((int64_t)head * a.n_blocks + c) * (kBlock * kDim);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int task = tid + kThreads * j;
+    const int dp = task >> 4, cc = task & 15;
+    const int kb = 16 * (cc >> 1) + 4 * (cc & 1);
+    uint32_t lo[4], hi[4];
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const int k0 = kb + 8 * (e >> 2) + (e & 3);
+      const uint32_t v0 = *reinterpret_cast<const uint32_t*>(tile + k0 * kPitch + dp * 4);
+      const uint32_t v1 = *reinterpret_cast<const uint32_t*>(tile + (k0 + 1) * kPitch + dp * 4);
+      lo[e >> 1] = (v0 & 0xffffu) | (v1 << 16);            // column 2dp
+      hi[e >> 1] = (v0 >> 16) | (v1 & 0xffff0000u);        // column 2dp + 1
+    }
+    *reinterpret_cast<u32x4*>(dst + (2 * dp) * kBlock + cc * 8) = u32x4{lo[0], lo[1], lo[2], lo[3]};
+    *reinterpret_cast<u32x4*>(dst + (2 * dp + 1) * kBlock + cc * 8) = u32x4{hi[0], hi[1], hi[2], hi[3]};
+  }
+}
+
+hipError_t launch_v_transpose(const VtArgs& a, hipStream_t stream) {
+  const int64_t items = (int64_t)a.heads * a.n_blocks;
+  if (items <= 0) return hipSuccess;
+  hipLaunchKernelGGL(v_transpose_kernel, dim3((unsigned)items), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream) {

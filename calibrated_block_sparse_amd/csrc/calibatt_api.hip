@@ -63,18 +63,29 @@ extern "C" {
 
 const char* calibatt_last_error(void) { return g_last_error.c_str(); }
 
-int32_t calibatt_abi_version(void) { return 1; }
+int32_t calibatt_abi_version(void) { return 2; }
+
+size_t calibatt_sparse_attn_fwd_workspace(int32_t heads, int32_t n_tokens) {
+  if (heads <= 0 || n_tokens <= 0) return 0;
+  return (size_t)heads * (size_t)ceil_div(n_tokens, CALIBATT_BLOCK) * CALIBATT_BLOCK *
+         CALIBATT_HEAD_DIM * 2;
+}
 
 int calibatt_sparse_attn_fwd(const void* q, const void* k, const void* v, void* o, int32_t heads,
                              int32_t n_tokens, int32_t head_dim, int64_t stride_head,
                              int64_t stride_token, float scale, const int32_t* kv_offsets,
                              const int32_t* kv_indices, int64_t nnz,
                              const uint8_t* repeat_flags, const calibatt_grid* grid,
-                             void* stream) {
+                             void* workspace, size_t workspace_bytes, void* stream) {
   const char* fn = "calibatt_sparse_attn_fwd";
   int rc = check_tensor_layout(fn, heads, n_tokens, head_dim, stride_head, stride_token);
   if (rc) return rc;
   if (heads == 0 || n_tokens == 0) return ok();
+  const size_t need = calibatt_sparse_attn_fwd_workspace(heads, n_tokens);
+  if (!workspace || workspace_bytes < need)
+    return fail(CALIBATT_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu", fn, workspace_bytes, need);
+  if (reinterpret_cast<uintptr_t>(workspace) & 15u)
+    return fail(CALIBATT_ERR_WORKSPACE, "%s: workspace must be 16-byte aligned", fn);
   if (!q || !k || !v || !o) return fail(CALIBATT_ERR_INVALID_ARG, "%s: null q/k/v/o", fn);
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
     return fail(CALIBATT_ERR_INVALID_ARG, "%s: q/k/v/o must be 16-byte aligned", fn);
@@ -110,6 +121,7 @@ int calibatt_sparse_attn_fwd(const void* q, const void* k, const void* v, void* 
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
   a.v = static_cast<const uint16_t*>(v);
+  a.vt = static_cast<const uint16_t*>(workspace);
   a.o = static_cast<uint16_t*>(o);
   a.stride_head = stride_head;
   a.stride_token = stride_token;
@@ -120,6 +132,19 @@ int calibatt_sparse_attn_fwd(const void* q, const void* k, const void* v, void* 
   a.n_tokens = n_tokens;
   a.n_blocks = R;
   a.rep_tiles = (int32_t)ceil_div(a.anchor_queries, CALIBATT_BLOCK);
+
+  if ((int64_t)heads * R > 0x7fffffff) return fail(CALIBATT_ERR_UNSUPPORTED, "%s: too many tiles", fn);
+  // V^T tiles of every head into the workspace, then the attention.
+  VtArgs t;
+  t.v = a.v;
+  t.vt = static_cast<uint16_t*>(workspace);
+  t.stride_head = stride_head;
+  t.stride_token = stride_token;
+  t.heads = heads;
+  t.n_tokens = n_tokens;
+  t.n_blocks = R;
+  hipError_t te = launch_v_transpose(t, static_cast<hipStream_t>(stream));
+  if (te != hipSuccess) return hip_fail(te, fn);
 
   // Launch in chunks of at most kMaxHeadsPerLaunch heads; repeat heads (the
   // longest tiles) come first in each launch.

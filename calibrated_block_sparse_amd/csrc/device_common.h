@@ -30,6 +30,7 @@ constexpr int kLdsStride = 136;   // bf16 per LDS tile row: 256 B + 16 B pad
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -38,9 +39,13 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // ids this map hands each XCD S consecutive work items, so the tiles that
 // share an XCD's L2 at a given time are neighbouring query blocks of one
 // head and reuse the same key/value blocks. The last partial run is left in
-// order.
+// order. S = CALIBATT_XCD_RUN (0 disables the remap).
+#ifndef CALIBATT_XCD_RUN
+#define CALIBATT_XCD_RUN 32
+#endif
 __device__ __forceinline__ int xcd_remap(int id, int n_items) {
-  constexpr int kXcd = 8, kPer = 32, kSpan = kXcd * kPer;
+  constexpr int kXcd = 8, kPer = CALIBATT_XCD_RUN, kSpan = kXcd * kPer;
+  if (kPer == 0) return id;
   const int base = (id / kSpan) * kSpan;
   if (base + kSpan > n_items) return id;
   const int local = id - base;
@@ -190,17 +195,21 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
+// Wave-uniform value pinned to a scalar register (asm "s" operands would
+// otherwise print a vector register the compiler chose to keep it in).
+__device__ __forceinline__ uint32_t uni(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+
 // 16 bytes per lane from sbase + voff into LDS [lds + 16*lane]. sbase and lds
 // must be wave-uniform.
 __device__ __forceinline__ void copy16_saddr(uint32_t lds, const void* sbase, uint32_t voff) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :: "s"(lds), "v"(voff), "s"(sbase) : "memory", "m0");
+               :: "s"(uni(lds)), "v"(voff), "s"(sbase) : "memory", "m0");
 }
 
 // Same with a per-lane 64-bit address.
 __device__ __forceinline__ void copy16_vaddr(uint32_t lds, const void* vaddr) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-               :: "s"(lds), "v"(vaddr) : "memory", "m0");
+               :: "s"(uni(lds)), "v"(vaddr) : "memory", "m0");
 }
 
 #pragma clang diagnostic pop
@@ -217,45 +226,123 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Per-lane source offsets of the fast (unclamped) copy path, fixed for the
-// kernel: K needs one per j % 4 (its swizzle repeats every 16 rows), V one.
+// Per-lane source offsets of the fast copy path, fixed for the kernel.
+// Instruction j of a wave covers rows 32w + 4j + sub (sub = lane / 16) with
+// physical chunk p = lane % 16. K swizzles chunks by (row % 16) = 4(j%4) + sub:
+// logical chunk p ^ sub ^ 4(j%4), i.e. the j = 0 offset with bits 6-7 flipped
+// by (j%4) << 6 -- valid while a row's byte offset has zero low 8 bits, so the
+// fast path requires row_bytes % 256 == 0 (other strides take the per-lane
+// path). V swizzles by 4*(row % 4) = 4*sub, the same for every j.
 struct CopyPlan {
-  uint32_t k_off[4];
-  uint32_t v_off;
+  uint32_t k_off;      // row sub, chunk p ^ sub
+  uint32_t v_off;      // row sub, chunk p ^ 4*sub
   int64_t row_bytes;   // stride_token * 2
+  bool fast;           // row_bytes % 256 == 0
 };
 
 __device__ __forceinline__ CopyPlan make_copy_plan(int64_t stride_token, int lane) {
   CopyPlan cp;
   const int sub = lane >> 4, p = lane & 15;
   cp.row_bytes = stride_token * 2;
-#pragma unroll
-  for (int jm = 0; jm < 4; ++jm) {
-    const int r = 4 * jm + sub;  // row modulo 16
-    cp.k_off[jm] = (uint32_t)(r * cp.row_bytes + ((p ^ r) << 4));
-  }
+  cp.k_off = (uint32_t)(sub * cp.row_bytes + ((p ^ sub) << 4));
   cp.v_off = (uint32_t)(sub * cp.row_bytes + ((p ^ (sub << 2)) << 4));
+  cp.fast = (cp.row_bytes & 255) == 0;
   return cp;
 }
 
+// Buffer resource over `base` with the largest record count (the fast copy
+// path only addresses rows that exist; the range check never fires).
+__device__ __forceinline__ u32x4 make_rsrc(const void* base) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  u32x4 r;
+  r[0] = uni((uint32_t)a);
+  r[1] = uni((uint32_t)(a >> 32) & 0xffffu);  // stride 0 (raw buffer)
+  r[2] = 0xffffffffu;
+  r[3] = 0x00020000u;                          // untyped 32-bit data
+  return r;
+}
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+
+// Eight copies of rows 32*wave .. +31 of a full K tile (rsrc over the
+// tile's first row, soff = byte offset of row 32*wave). Instruction j reads
+// with offset k ^ ((j % 4) << 6) at row base 32*wave + 4j.
+__device__ __forceinline__ void copy_k_fast(uint32_t lds, u32x4 rs, uint32_t soff, uint32_t step4,
+                                            uint32_t k) {
+  uint32_t t0, t1;
+  asm volatile(
+      "s_mov_b32 m0, %[lds]\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %[k], %[rs], %[so] offen lds\n\t"
+      "v_xor_b32 %[t0], 0x40, %[k]\n\t"
+      "s_add_u32 %[so], %[so], %[st]\n\ts_add_u32 m0, m0, 0x400\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %[t0], %[rs], %[so] offen lds\n\t"
+      "v_xor_b32 %[t1], 0x80, %[k]\n\t"
+      "s_add_u32 %[so], %[so], %[st]\n\ts_add_u32 m0, m0, 0x400\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %[t1], %[rs], %[so] offen lds\n\t"
+      "v_xor_b32 %[t0], 0xc0, %[k]\n\t"
+      "s_add_u32 %[so], %[so], %[st]\n\ts_add_u32 m0, m0, 0x400\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %[t0], %[rs], %[so] offen lds\n\t"
+      "s_add_u32 %[so], %[so], %[st]\n\ts_add_u32 m0, m0, 0x400\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %[k], %[rs], %[so] offen lds\n\t"
+      "v_xor_b32 %[t1], 0x40, %[k]\n\t"
+      "s_add_u32 %[so], %[so], %[st]\n\ts_add_u32 m0, m0, 0x400\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %[t1], %[rs], %[so] offen lds\n\t"
+      "v_xor_b32 %[t0], 0x80, %[k]\n\t"
+      "s_add_u32 %[so], %[so], %[st]\n\ts_add_u32 m0, m0, 0x400\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %[t0], %[rs], %[so] offen lds\n\t"
+      "v_xor_b32 %[t1], 0xc0, %[k]\n\t"
+      "s_add_u32 %[so], %[so], %[st]\n\ts_add_u32 m0, m0, 0x400\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %[t1], %[rs], %[so] offen lds"
+      : [so] "+s"(soff), [t0] "=&v"(t0), [t1] "=&v"(t1)
+      : [lds] "s"(uni(lds)), [rs] "s"(rs), [st] "s"(uni(step4)), [k] "v"(k)
+      : "memory", "m0", "scc");
+}
+
+// Eight copies of rows 32*wave .. +31 of a full V tile; the row base
+// advances 4 rows per instruction.
+__device__ __forceinline__ void copy_v_fast(uint32_t lds, u32x4 rs, uint32_t soff, uint32_t step4,
+                                            uint32_t v) {
+  asm volatile(
+      "s_mov_b32 m0, %[lds]\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %[v], %[rs], %[so] offen lds\n\t"
+      "s_add_u32 %[so], %[so], %[st]\n\ts_add_u32 m0, m0, 0x400\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %[v], %[rs], %[so] offen lds\n\t"
+      "s_add_u32 %[so], %[so], %[st]\n\ts_add_u32 m0, m0, 0x400\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %[v], %[rs], %[so] offen lds\n\t"
+      "s_add_u32 %[so], %[so], %[st]\n\ts_add_u32 m0, m0, 0x400\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %[v], %[rs], %[so] offen lds\n\t"
+      "s_add_u32 %[so], %[so], %[st]\n\ts_add_u32 m0, m0, 0x400\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %[v], %[rs], %[so] offen lds\n\t"
+      "s_add_u32 %[so], %[so], %[st]\n\ts_add_u32 m0, m0, 0x400\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %[v], %[rs], %[so] offen lds\n\t"
+      "s_add_u32 %[so], %[so], %[st]\n\ts_add_u32 m0, m0, 0x400\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %[v], %[rs], %[so] offen lds\n\t"
+      "s_add_u32 %[so], %[so], %[st]\n\ts_add_u32 m0, m0, 0x400\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %[v], %[rs], %[so] offen lds"
+      : [so] "+s"(soff)
+      : [lds] "s"(uni(lds)), [rs] "s"(rs), [st] "s"(uni(step4)), [v] "v"(v)
+      : "memory", "m0", "scc");
+}
+
+#pragma clang diagnostic pop
+
 // Issues this wave's eight copies of the tile whose first token row is key0
 // (kIsV selects the V swizzle). Rows at or past n_tokens are read from row
-// n_tokens - 1 instead (their keys are masked out of the softmax, so those
-// values never matter).
+// n_tokens - 1 instead (their scores repeat a real score of the block and
+// their probabilities are zeroed, so those values never matter).
 template <bool kIsV>
 __device__ __forceinline__ void copy_tile(uint32_t lds_tile, const uint16_t* __restrict__ src,
                                           const CopyPlan& cp, int key0, int n_tokens, int wave,
                                           int lane) {
   const uint32_t lds = lds_tile + wave * (kCopiesPerTile * 1024);
-  if (key0 + kBlock <= n_tokens) {
-    const char* base = reinterpret_cast<const char*>(src) + (int64_t)(key0 + 32 * wave) * cp.row_bytes;
-#pragma unroll
-    for (int j = 0; j < kCopiesPerTile; ++j) {
-      if (kIsV)
-        copy16_saddr(lds + 1024 * j, base + (int64_t)(4 * j) * cp.row_bytes, cp.v_off);
-      else
-        copy16_saddr(lds + 1024 * j, base + (int64_t)(16 * (j >> 2)) * cp.row_bytes, cp.k_off[j & 3]);
-    }
+  if (cp.fast && key0 + kBlock <= n_tokens) {
+    const u32x4 rs = make_rsrc(reinterpret_cast<const char*>(src) + (int64_t)key0 * cp.row_bytes);
+    const uint32_t soff = uni((uint32_t)(32 * wave) * (uint32_t)cp.row_bytes);
+    if (kIsV)
+      copy_v_fast(lds, rs, soff, 4u * (uint32_t)cp.row_bytes, cp.v_off);
+    else
+      copy_k_fast(lds, rs, soff, 4u * (uint32_t)cp.row_bytes, cp.k_off);
   } else {
     const int sub = lane >> 4, p = lane & 15;
 #pragma unroll
@@ -288,6 +375,23 @@ __device__ __forceinline__ int v_operand_offset(int u, int lane) {
   const int row = 4 * (j >> 1) + m;
   const int chunk = (4 * u + 2 * (j & 1) + (q >> 1)) ^ (4 * m);
   return row * 256 + chunk * 16 + (q & 1) * 8;
+}
+
+typedef __attribute__((address_space(3))) const uint8_t* lds_cptr;
+
+// LDS loads at an LDS byte address. Callers pass a per-lane base plus a
+// compile-time displacement, which the compiler folds into the instruction's
+// 16-bit offset field (so one base register serves many loads).
+__device__ __forceinline__ bf16x8 lds_read_b128(uint32_t addr) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>((lds_cptr)(uintptr_t)addr);
+}
+
+__device__ __forceinline__ bf16x8 lds_read_v_operand(uint32_t addr) {
+  typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(uintptr_t)addr);
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(uintptr_t)(addr + 2048));
+  const bf16x4 a = __builtin_bit_cast(bf16x4, lo), b = __builtin_bit_cast(bf16x4, hi);
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 __device__ __forceinline__ bf16x8 v_operand(const uint8_t* vtile, int off) {

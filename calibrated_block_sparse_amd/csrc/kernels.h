@@ -13,6 +13,7 @@ struct AttnArgs {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
+  const uint16_t* vt;        // V^T tiles [heads][R][128 d][128 keys] (workspace)
   uint16_t* o;
   int64_t stride_head;
   int64_t stride_token;
@@ -31,6 +32,16 @@ struct AttnArgs {
   int32_t heads[kMaxHeadsPerLaunch];
 };
 
+struct VtArgs {
+  const uint16_t* v;
+  uint16_t* vt;
+  int64_t stride_head;
+  int64_t stride_token;
+  int32_t heads;
+  int32_t n_tokens;
+  int32_t n_blocks;
+};
+
 struct EnergyArgs {
   const uint16_t* q;
   const uint16_t* k;
@@ -45,6 +56,7 @@ struct EnergyArgs {
   int32_t heads;
 };
 
+hipError_t launch_v_transpose(const VtArgs& a, hipStream_t stream);
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_block_energy(const EnergyArgs& a, hipStream_t stream);
 

@@ -63,7 +63,8 @@ typedef struct calibatt_grid {
 /* Message of the last failed call on this thread ("" if none). */
 const char* calibatt_last_error(void);
 
-/* Interface version (increments on any change of this header). */
+/* Interface version (increments on any change of this header). Version 2
+ * added the workspace of calibatt_sparse_attn_fwd. */
 int32_t calibatt_abi_version(void);
 
 /*
@@ -96,15 +97,30 @@ int32_t calibatt_abi_version(void);
  *   repeat_flags host uint8 [heads] or NULL (no repeat heads)
  *   grid         host pointer, required iff a repeat flag is set:
  *                frames*rows*cols == N and 1 <= anchors <= rows
+ *   workspace    device, 16-byte aligned, at least
+ *                calibatt_sparse_attn_fwd_workspace(heads, N) bytes; the call
+ *                first writes V there as [heads][R][128 d][128 keys] tiles
+ *                (transposed per key block, zero past N) and the attention
+ *                reads V only from there. Its contents after the call are
+ *                unspecified; calls sharing one workspace must not overlap.
  * kv_offsets / kv_indices may be NULL when every head repeats.
- * heads == 0 or N == 0 is a no-op.
+ * heads == 0 or N == 0 is a no-op. A workspace that is missing, too small or
+ * misaligned gives CALIBATT_ERR_WORKSPACE.
  */
 int calibatt_sparse_attn_fwd(const void* q, const void* k, const void* v, void* o,
                              int32_t heads, int32_t n_tokens, int32_t head_dim,
                              int64_t stride_head, int64_t stride_token, float scale,
                              const int32_t* kv_offsets, const int32_t* kv_indices,
                              int64_t nnz, const uint8_t* repeat_flags,
-                             const calibatt_grid* grid, void* stream);
+                             const calibatt_grid* grid, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of device workspace calibatt_sparse_attn_fwd needs: heads * R *
+ * 128 * 128 * 2 (one bf16 V^T tile per head and key block). 0 when heads or
+ * n_tokens is not positive.
+ */
+size_t calibatt_sparse_attn_fwd_workspace(int32_t heads, int32_t n_tokens);
 
 /*
  * Bytes of device workspace calibatt_block_energy needs (row statistics:

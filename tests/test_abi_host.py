@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version(lib):
-    assert cbs.calibatt_abi_version() == 1
+    assert cbs.calibatt_abi_version() == 2
 
 
 def fake(n=16):
@@ -46,12 +46,25 @@ def fake(n=16):
 
 def attn(lib, **kw):
     args = dict(q=fake(), k=fake(), v=fake(), o=fake(), heads=2, n=1024, d=128, sh=1024 * 128,
-                stok=128, scale=0.088, off=fake(), idx=fake(), nnz=10, flags=None, grid=None)
+                stok=128, scale=0.088, off=fake(), idx=fake(), nnz=10, flags=None, grid=None,
+                ws=fake(), wsb=cbs.calibatt_sparse_attn_fwd_workspace(2, 1024))
     args.update(kw)
     return lib.calibatt_sparse_attn_fwd(args["q"], args["k"], args["v"], args["o"], args["heads"],
                                         args["n"], args["d"], args["sh"], args["stok"], args["scale"],
                                         args["off"], args["idx"], args["nnz"], args["flags"],
-                                        args["grid"], None)
+                                        args["grid"], args["ws"], args["wsb"], None)
+
+
+def test_attention_workspace(lib):
+    # one bf16 128 x 128 V^T tile per head and key block (R = ceil(N / 128))
+    assert cbs.calibatt_sparse_attn_fwd_workspace(2, 1024) == 2 * 8 * 128 * 128 * 2
+    assert cbs.calibatt_sparse_attn_fwd_workspace(40, 75600) == 40 * 591 * 128 * 128 * 2
+    assert cbs.calibatt_sparse_attn_fwd_workspace(0, 100) == 0
+    need = cbs.calibatt_sparse_attn_fwd_workspace(2, 1024)
+    assert attn(lib, ws=None) == -4
+    assert "workspace" in cbs.calibatt_last_error()
+    assert attn(lib, wsb=need - 1) == -4
+    assert attn(lib, ws=ctypes.c_void_p(4096 + 8)) == -4
 
 
 def test_attention_argument_errors(lib):
