@@ -34,6 +34,11 @@ SIGNATURES = {
                                             _c.c_int64, _c.c_int64, _c.c_float, _p, _p,
                                             _c.c_int64, _p, _p, _p, _c.c_size_t, _p]),
     "calibatt_sparse_attn_fwd_workspace": (_c.c_size_t, [_c.c_int32, _c.c_int32]),
+    "calibatt_prepare_vt": (_c.c_int, [_p, _c.c_int32, _c.c_int32, _c.c_int32, _c.c_int64,
+                                       _c.c_int64, _p, _c.c_size_t, _p]),
+    "calibatt_sparse_attn_fwd_vt": (_c.c_int, [_p, _p, _p, _p, _c.c_int32, _c.c_int32,
+                                               _c.c_int32, _c.c_int64, _c.c_int64, _c.c_float,
+                                               _p, _p, _c.c_int64, _p, _p, _c.c_size_t, _p]),
     "calibatt_block_energy_workspace": (_c.c_size_t, [_c.c_int32, _c.c_int32]),
     "calibatt_block_energy": (_c.c_int, [_p, _p, _p, _c.c_int32, _c.c_int32, _c.c_int32,
                                          _c.c_int64, _c.c_int64, _c.c_float, _p, _c.c_size_t, _p]),
@@ -161,6 +166,41 @@ def calibatt_sparse_attn_fwd(q, k, v, o, kv_offsets, kv_indices, scale: float,
                                       workspace.numel() * workspace.element_size(),
                                       _stream(stream))
     _check("calibatt_sparse_attn_fwd", rc)
+
+
+def _flags_grid(H, repeat_flags, grid):
+    flags = None
+    if repeat_flags is not None:
+        arr = np.ascontiguousarray(np.asarray(repeat_flags, dtype=np.uint8))
+        if arr.shape != (H,):
+            raise ValueError("repeat_flags must have one entry per head")
+        flags = arr
+    g = None if grid is None else Grid(*[int(x) for x in grid])
+    return flags, g
+
+
+def calibatt_prepare_vt(v, workspace, stream=None) -> None:
+    """workspace (uint8 CUDA, calibatt_sparse_attn_fwd_workspace bytes) <- the
+    V^T tiles of v ([H][N][128] bf16 CUDA)."""
+    H, N, D, sh, stok = _attn_layout("calibatt_prepare_vt", v)
+    rc = load_library().calibatt_prepare_vt(_ptr(v), H, N, D, sh, stok, _ptr(workspace),
+                                            workspace.numel() * workspace.element_size(),
+                                            _stream(stream))
+    _check("calibatt_prepare_vt", rc)
+
+
+def calibatt_sparse_attn_fwd_vt(q, k, vt, o, kv_offsets, kv_indices, scale: float,
+                                repeat_flags=None, grid=None, stream=None) -> None:
+    """o <- block-sparse attention of q, k and the V^T tiles in vt (filled by
+    calibatt_prepare_vt); otherwise as calibatt_sparse_attn_fwd."""
+    H, N, D, sh, stok = _attn_layout("calibatt_sparse_attn_fwd_vt", q, k, o)
+    nnz = 0 if kv_indices is None else kv_indices.numel()
+    flags, g = _flags_grid(H, repeat_flags, grid)
+    rc = load_library().calibatt_sparse_attn_fwd_vt(
+        _ptr(q), _ptr(k), _ptr(vt), _ptr(o), H, N, D, sh, stok, float(scale), _ptr(kv_offsets),
+        _ptr(kv_indices), nnz, None if flags is None else flags.ctypes.data_as(ctypes.c_void_p),
+        None if g is None else ctypes.byref(g), vt.numel() * vt.element_size(), _stream(stream))
+    _check("calibatt_sparse_attn_fwd_vt", rc)
 
 
 def calibatt_block_energy_workspace(heads: int, n_tokens: int) -> int:

@@ -63,7 +63,8 @@ extern "C" {
 
 const char* calibatt_last_error(void) { return g_last_error.c_str(); }
 
-int32_t calibatt_abi_version(void) { return 2; }
+int32_t calibatt_abi_version(void) { return 3; }
+
 
 size_t calibatt_sparse_attn_fwd_workspace(int32_t heads, int32_t n_tokens) {
   if (heads <= 0 || n_tokens <= 0) return 0;
@@ -71,29 +72,21 @@ size_t calibatt_sparse_attn_fwd_workspace(int32_t heads, int32_t n_tokens) {
          CALIBATT_HEAD_DIM * 2;
 }
 
-int calibatt_sparse_attn_fwd(const void* q, const void* k, const void* v, void* o, int32_t heads,
-                             int32_t n_tokens, int32_t head_dim, int64_t stride_head,
-                             int64_t stride_token, float scale, const int32_t* kv_offsets,
-                             const int32_t* kv_indices, int64_t nnz,
-                             const uint8_t* repeat_flags, const calibatt_grid* grid,
-                             void* workspace, size_t workspace_bytes, void* stream) {
-  const char* fn = "calibatt_sparse_attn_fwd";
-  int rc = check_tensor_layout(fn, heads, n_tokens, head_dim, stride_head, stride_token);
-  if (rc) return rc;
-  if (heads == 0 || n_tokens == 0) return ok();
-  const size_t need = calibatt_sparse_attn_fwd_workspace(heads, n_tokens);
-  if (!workspace || workspace_bytes < need)
-    return fail(CALIBATT_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu", fn, workspace_bytes, need);
-  if (reinterpret_cast<uintptr_t>(workspace) & 15u)
-    return fail(CALIBATT_ERR_WORKSPACE, "%s: workspace must be 16-byte aligned", fn);
-  if (!q || !k || !v || !o) return fail(CALIBATT_ERR_INVALID_ARG, "%s: null q/k/v/o", fn);
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
-    return fail(CALIBATT_ERR_INVALID_ARG, "%s: q/k/v/o must be 16-byte aligned", fn);
+// Attention launches over V^T tiles already in `vt` (no validation of vt's
+// contents). Shared by calibatt_sparse_attn_fwd and _fwd_vt.
+static int attn_core(const char* fn, const void* q, const void* k, const void* vt, void* o,
+                     int32_t heads, int32_t n_tokens, int64_t stride_head, int64_t stride_token,
+                     float scale, const int32_t* kv_offsets, const int32_t* kv_indices, int64_t nnz,
+                     const uint8_t* repeat_flags, const calibatt_grid* grid, hipStream_t stream) {
+  if (!q || !k || !o) return fail(CALIBATT_ERR_INVALID_ARG, "%s: null q/k/o", fn);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(o))
+    return fail(CALIBATT_ERR_INVALID_ARG, "%s: q/k/o must be 16-byte aligned", fn);
   if (!(scale > 0.f) || !std::isfinite(scale))
     return fail(CALIBATT_ERR_INVALID_ARG, "%s: scale must be finite and > 0", fn);
   if (nnz < 0) return fail(CALIBATT_ERR_INVALID_ARG, "%s: nnz < 0", fn);
 
   const int32_t R = (int32_t)ceil_div(n_tokens, CALIBATT_BLOCK);
+  if ((int64_t)heads * R > 0x7fffffff) return fail(CALIBATT_ERR_UNSUPPORTED, "%s: too many tiles", fn);
   std::vector<int32_t> rep_heads, sparse_heads;
   for (int32_t h = 0; h < heads; ++h)
     (repeat_flags && repeat_flags[h] ? rep_heads : sparse_heads).push_back(h);
@@ -120,8 +113,7 @@ int calibatt_sparse_attn_fwd(const void* q, const void* k, const void* v, void* 
 
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
-  a.v = static_cast<const uint16_t*>(v);
-  a.vt = static_cast<const uint16_t*>(workspace);
+  a.vt = static_cast<const uint16_t*>(vt);
   a.o = static_cast<uint16_t*>(o);
   a.stride_head = stride_head;
   a.stride_token = stride_token;
@@ -132,19 +124,6 @@ int calibatt_sparse_attn_fwd(const void* q, const void* k, const void* v, void* 
   a.n_tokens = n_tokens;
   a.n_blocks = R;
   a.rep_tiles = (int32_t)ceil_div(a.anchor_queries, CALIBATT_BLOCK);
-
-  if ((int64_t)heads * R > 0x7fffffff) return fail(CALIBATT_ERR_UNSUPPORTED, "%s: too many tiles", fn);
-  // V^T tiles of every head into the workspace, then the attention.
-  VtArgs t;
-  t.v = a.v;
-  t.vt = static_cast<uint16_t*>(workspace);
-  t.stride_head = stride_head;
-  t.stride_token = stride_token;
-  t.heads = heads;
-  t.n_tokens = n_tokens;
-  t.n_blocks = R;
-  hipError_t te = launch_v_transpose(t, static_cast<hipStream_t>(stream));
-  if (te != hipSuccess) return hip_fail(te, fn);
 
   // Launch in chunks of at most kMaxHeadsPerLaunch heads; repeat heads (the
   // longest tiles) come first in each launch.
@@ -158,10 +137,104 @@ int calibatt_sparse_attn_fwd(const void* q, const void* k, const void* v, void* 
     const int64_t items = (int64_t)a.n_rep * a.rep_tiles + (int64_t)a.n_sparse * R;
     if (items > 0x7fffffff) return fail(CALIBATT_ERR_UNSUPPORTED, "%s: too many tiles", fn);
     a.n_items = (int32_t)items;
-    hipError_t e = launch_attn_fwd(a, static_cast<hipStream_t>(stream));
+    hipError_t e = launch_attn_fwd(a, stream);
     if (e != hipSuccess) return hip_fail(e, fn);
   }
   return ok();
+}
+
+static int check_workspace(const char* fn, int32_t heads, int32_t n_tokens, const void* ws,
+                           size_t ws_bytes) {
+  const size_t need = calibatt_sparse_attn_fwd_workspace(heads, n_tokens);
+  if (!ws || ws_bytes < need)
+    return fail(CALIBATT_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu", fn, ws_bytes, need);
+  if (reinterpret_cast<uintptr_t>(ws) & 15u)
+    return fail(CALIBATT_ERR_WORKSPACE, "%s: workspace must be 16-byte aligned", fn);
+  return CALIBATT_OK;
+}
+
+int calibatt_prepare_vt(const void* v, int32_t heads, int32_t n_tokens, int32_t head_dim,
+                        int64_t stride_head, int64_t stride_token, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  const char* fn = "calibatt_prepare_vt";
+  int rc = check_tensor_layout(fn, heads, n_tokens, head_dim, stride_head, stride_token);
+  if (rc) return rc;
+  if (heads == 0 || n_tokens == 0) return ok();
+  rc = check_workspace(fn, heads, n_tokens, workspace, workspace_bytes);
+  if (rc) return rc;
+  if (!v) return fail(CALIBATT_ERR_INVALID_ARG, "%s: null v", fn);
+  if (!aligned16(v)) return fail(CALIBATT_ERR_INVALID_ARG, "%s: v must be 16-byte aligned", fn);
+  const int32_t R = (int32_t)ceil_div(n_tokens, CALIBATT_BLOCK);
+  if ((int64_t)heads * R > 0x7fffffff) return fail(CALIBATT_ERR_UNSUPPORTED, "%s: too many tiles", fn);
+  VtArgs t;
+  t.v = static_cast<const uint16_t*>(v);
+  t.vt = static_cast<uint16_t*>(workspace);
+  t.stride_head = stride_head;
+  t.stride_token = stride_token;
+  t.heads = heads;
+  t.n_tokens = n_tokens;
+  t.n_blocks = R;
+  hipError_t e = launch_v_transpose(t, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return ok();
+}
+
+int calibatt_sparse_attn_fwd_vt(const void* q, const void* k, const void* vt, void* o,
+                                int32_t heads, int32_t n_tokens, int32_t head_dim,
+                                int64_t stride_head, int64_t stride_token, float scale,
+                                const int32_t* kv_offsets, const int32_t* kv_indices, int64_t nnz,
+                                const uint8_t* repeat_flags, const calibatt_grid* grid,
+                                size_t vt_bytes, void* stream) {
+  const char* fn = "calibatt_sparse_attn_fwd_vt";
+  int rc = check_tensor_layout(fn, heads, n_tokens, head_dim, stride_head, stride_token);
+  if (rc) return rc;
+  if (heads == 0 || n_tokens == 0) return ok();
+  rc = check_workspace(fn, heads, n_tokens, vt, vt_bytes);
+  if (rc) return rc;
+  return attn_core(fn, q, k, vt, o, heads, n_tokens, stride_head, stride_token, scale, kv_offsets,
+                   kv_indices, nnz, repeat_flags, grid, static_cast<hipStream_t>(stream));
+}
+
+int calibatt_sparse_attn_fwd(const void* q, const void* k, const void* v, void* o, int32_t heads,
+                             int32_t n_tokens, int32_t head_dim, int64_t stride_head,
+                             int64_t stride_token, float scale, const int32_t* kv_offsets,
+                             const int32_t* kv_indices, int64_t nnz,
+                             const uint8_t* repeat_flags, const calibatt_grid* grid,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "calibatt_sparse_attn_fwd";
+  int rc = check_tensor_layout(fn, heads, n_tokens, head_dim, stride_head, stride_token);
+  if (rc) return rc;
+  if (heads == 0 || n_tokens == 0) return ok();
+  rc = check_workspace(fn, heads, n_tokens, workspace, workspace_bytes);
+  if (rc) return rc;
+  if (!v) return fail(CALIBATT_ERR_INVALID_ARG, "%s: null q/k/v/o", fn);
+  if (!aligned16(v)) return fail(CALIBATT_ERR_INVALID_ARG, "%s: q/k/v/o must be 16-byte aligned", fn);
+  // validate everything the attention needs before enqueuing the pre-pass
+  if (!q || !k || !o) return fail(CALIBATT_ERR_INVALID_ARG, "%s: null q/k/v/o", fn);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(o))
+    return fail(CALIBATT_ERR_INVALID_ARG, "%s: q/k/v/o must be 16-byte aligned", fn);
+  if (!(scale > 0.f) || !std::isfinite(scale))
+    return fail(CALIBATT_ERR_INVALID_ARG, "%s: scale must be finite and > 0", fn);
+  if (nnz < 0) return fail(CALIBATT_ERR_INVALID_ARG, "%s: nnz < 0", fn);
+  bool any_rep = false, any_sparse = false;
+  for (int32_t h = 0; h < heads; ++h) (repeat_flags && repeat_flags[h] ? any_rep : any_sparse) = true;
+  if (any_rep) {
+    if (!grid) return fail(CALIBATT_ERR_INVALID_ARG, "%s: repeat heads need a grid", fn);
+    if (grid->frames <= 0 || grid->rows <= 0 || grid->cols <= 0 ||
+        (int64_t)grid->frames * grid->rows * grid->cols != n_tokens)
+      return fail(CALIBATT_ERR_INVALID_ARG, "%s: grid %dx%dx%d does not cover N=%d", fn,
+                  grid->frames, grid->rows, grid->cols, n_tokens);
+    if (grid->anchors < 1 || grid->anchors > grid->rows)
+      return fail(CALIBATT_ERR_INVALID_ARG, "%s: anchors %d not in [1, rows=%d]", fn,
+                  grid->anchors, grid->rows);
+  }
+  if (any_sparse && (!kv_offsets || (!kv_indices && nnz > 0)))
+    return fail(CALIBATT_ERR_INVALID_ARG, "%s: null kept-block list", fn);
+  rc = calibatt_prepare_vt(v, heads, n_tokens, head_dim, stride_head, stride_token, workspace,
+                           workspace_bytes, stream);
+  if (rc) return rc;
+  return attn_core(fn, q, k, workspace, o, heads, n_tokens, stride_head, stride_token, scale,
+                   kv_offsets, kv_indices, nnz, repeat_flags, grid, static_cast<hipStream_t>(stream));
 }
 
 size_t calibatt_block_energy_workspace(int32_t heads, int32_t n_tokens) {

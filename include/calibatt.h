@@ -64,7 +64,8 @@ typedef struct calibatt_grid {
 const char* calibatt_last_error(void);
 
 /* Interface version (increments on any change of this header). Version 2
- * added the workspace of calibatt_sparse_attn_fwd. */
+ * added the workspace of calibatt_sparse_attn_fwd, version 3 its two halves
+ * calibatt_prepare_vt and calibatt_sparse_attn_fwd_vt. */
 int32_t calibatt_abi_version(void);
 
 /*
@@ -121,6 +122,29 @@ int calibatt_sparse_attn_fwd(const void* q, const void* k, const void* v, void* 
  * n_tokens is not positive.
  */
 size_t calibatt_sparse_attn_fwd_workspace(int32_t heads, int32_t n_tokens);
+
+/*
+ * First half of calibatt_sparse_attn_fwd: writes the V^T tiles of v
+ * ([heads][N][128] bf16, strides as above) into workspace (layout and size
+ * as described there). Enqueued on `stream`; errors as for the full call.
+ */
+int calibatt_prepare_vt(const void* v, int32_t heads, int32_t n_tokens, int32_t head_dim,
+                        int64_t stride_head, int64_t stride_token, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/*
+ * Second half of calibatt_sparse_attn_fwd: the attention with V taken from
+ * vt, which calibatt_prepare_vt filled for the same heads and N (its
+ * contents are not checked). Arguments otherwise as for the full call; the
+ * results are identical bit for bit. For callers that prepare V^T on another
+ * stream or reuse it for several query sets.
+ */
+int calibatt_sparse_attn_fwd_vt(const void* q, const void* k, const void* vt, void* o,
+                                int32_t heads, int32_t n_tokens, int32_t head_dim,
+                                int64_t stride_head, int64_t stride_token, float scale,
+                                const int32_t* kv_offsets, const int32_t* kv_indices,
+                                int64_t nnz, const uint8_t* repeat_flags,
+                                const calibatt_grid* grid, size_t vt_bytes, void* stream);
 
 /*
  * Bytes of device workspace calibatt_block_energy needs (row statistics:

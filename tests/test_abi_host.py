@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version(lib):
-    assert cbs.calibatt_abi_version() == 2
+    assert cbs.calibatt_abi_version() == 3
 
 
 def fake(n=16):
@@ -65,6 +65,12 @@ def test_attention_workspace(lib):
     assert "workspace" in cbs.calibatt_last_error()
     assert attn(lib, wsb=need - 1) == -4
     assert attn(lib, ws=ctypes.c_void_p(4096 + 8)) == -4
+    # the two halves check the same workspace
+    assert lib.calibatt_prepare_vt(fake(), 2, 1024, 128, 1024 * 128, 128, fake(), need - 1, None) == -4
+    assert lib.calibatt_prepare_vt(None, 2, 1024, 128, 1024 * 128, 128, fake(), need, None) == -1
+    assert lib.calibatt_sparse_attn_fwd_vt(fake(), fake(), None, fake(), 2, 1024, 128, 1024 * 128,
+                                           128, 0.088, fake(), fake(), 10, None, None, need,
+                                           None) == -4
 
 
 def test_attention_argument_errors(lib):

@@ -139,6 +139,25 @@ def test_strided_layout(gpu):
     assert torch.equal(o_view.contiguous(), o_cont)
 
 
+def test_split_calls_match_full_call(gpu):
+    """calibatt_prepare_vt + calibatt_sparse_attn_fwd_vt give the full call's
+    output bit for bit, including repeat heads and a ragged tail."""
+    say("case split calls")
+    F, Hs, W, kk = 2, 30, 7, 5
+    N, H = F * Hs * W, 3
+    q, k, v = (gaussian_bf16(130 + i, (H, N, 128)).to(DEV) for i in range(3))
+    mask = bernoulli_mask(133, H, n_blocks(N), 0.5, diagonal=True)
+    flags = np.array([0, 1, 0], np.uint8)
+    off, idx = gpu.compile_skiplist(torch.from_numpy(mask).to(DEV))
+    o_full = gpu.sparse_attention(q, k, v, off, idx, 0.09, flags, (F, Hs, W, kk))
+    ws = torch.empty(gpu.calibatt_sparse_attn_fwd_workspace(H, N), dtype=torch.uint8, device=DEV)
+    gpu.calibatt_prepare_vt(v, ws)
+    o_split = torch.empty_like(q)
+    gpu.calibatt_sparse_attn_fwd_vt(q, k, ws, o_split, off, idx, 0.09, flags, (F, Hs, W, kk))
+    torch.cuda.synchronize()
+    assert torch.equal(o_full, o_split)
+
+
 @pytest.mark.parametrize("F,Hs,W,kk", [(2, 30, 7, 5), (3, 45, 4, 5), (2, 10, 13, 10), (1, 7, 9, 3)])
 def test_repeat_heads_small(gpu, F, Hs, W, kk):
     say(f"case repeat grid {F}x{Hs}x{W} k={kk}")
