@@ -44,6 +44,7 @@ namespace calibatt {
 // of reference exactly, so this saves the rescale of the output accumulator
 // on almost every block without changing the result.
 constexpr float kLazyRescaleLog2 = 8.f;
+constexpr float kLazyRescaleLimit = 256.f;  // 2^kLazyRescaleLog2
 
 // LDS operand reads kept in flight ahead of the MFMA that uses them.
 #ifndef CALIBATT_READ_DEPTH
@@ -190,19 +191,28 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const AttnArgs a)
     }
   };
 
-  // Probabilities of score tile t against the reference `mref` (16 per
-  // lane, as bf16), and the tile's running max into `mx`. Keys past the end
-  // of a ragged block were loaded as copies of key N-1, so their scores
-  // repeat a real score of the same block and leave the max unchanged;
-  // their probabilities are zeroed afterwards (zero_masked_probs).
-  auto probs_tile = [&](f32x16& sa, bf16x8& p_lo, bf16x8& p_hi, float mref, float& mx) {
+  // Probabilities of a score tile against the reference `mref` (16 per
+  // lane, as bf16), and their sum into `bsum` (the bf16-rounded values, two
+  // per dot instruction). Keys past the end of a ragged block were loaded as
+  // copies of key N-1 (their scores repeat a real score of the same block);
+  // their probabilities are zeroed and the sum redone afterwards.
+  auto probs_tile = [&](const f32x16& sa, bf16x8& p_lo, bf16x8& p_hi, float mref, float& bsum) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       p_lo[i] = (__bf16)fast_exp2(__builtin_fmaf(sa[i], sl, -mref));
       p_hi[i] = (__bf16)fast_exp2(__builtin_fmaf(sa[8 + i], sl, -mref));
     }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(mx, sa[i]);
+    const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+    float s0 = 0.f, s1 = 0.f;
+    s0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p_lo, p_lo, 0, 1), ones, s0, false);
+    s1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p_hi, p_hi, 0, 1), ones, s1, false);
+    s0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p_lo, p_lo, 2, 3), ones, s0, false);
+    s1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p_hi, p_hi, 2, 3), ones, s1, false);
+    s0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p_lo, p_lo, 4, 5), ones, s0, false);
+    s1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p_hi, p_hi, 4, 5), ones, s1, false);
+    s0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p_lo, p_lo, 6, 7), ones, s0, false);
+    s1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p_hi, p_hi, 6, 7), ones, s1, false);
+    bsum += s0 + s1;
     // Keep these exponentials next to the next tile's MFMAs: without this
     // use the compiler sinks them past the rescale test (whose rare path
     // recomputes them), where no MFMA is left to overlap them.
@@ -224,10 +234,10 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const AttnArgs a)
     }
   };
 
-  // Row sum of the bf16-rounded probabilities that enter P.V, so a dominant
-  // key's rounding cancels between numerator and denominator (it would not
-  // with a stale reference max). Two per dot instruction.
-  auto add_row_sum = [&](const bf16x8 (&pf)[8]) {
+  // Row sum (this lane's 64 keys) of the bf16-rounded probabilities that
+  // enter P.V, so a dominant key's rounding cancels between numerator and
+  // denominator (it would not with a stale reference max).
+  auto row_sum = [&](const bf16x8 (&pf)[8]) -> float {
     const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
     float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
@@ -237,7 +247,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const AttnArgs a)
       ls0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[s], pf[s], 4, 5), ones, ls0, false);
       ls1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[s], pf[s], 6, 7), ones, ls1, false);
     }
-    l_run += ls0 + ls1;
+    return ls0 + ls1;
   };
 
   // Zeroes the probabilities of keys at or past key_lim (ragged last block;
@@ -260,52 +270,59 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const AttnArgs a)
     }
   };
 
-  // Scores and probabilities of one block. The probabilities are computed
-  // against the current reference max before this block's max is known, so
-  // the exponentials of tile t overlap the MFMAs of tile t+1. The running
-  // max is only raised when the block's max exceeds it by more than
-  // 2^kLazyRescaleLog2 (first block, rarely later); then the output is
-  // rescaled and the block recomputed from the K tile still in LDS.
-  auto scores_probs = [&](bf16x8 (&pf)[8]) {
+  // Scores and probabilities of one block; returns this lane's sum of its
+  // probabilities. They are computed against the current reference max
+  // before anything about this block is known, so the exponentials of tile t
+  // overlap the MFMAs of tile t+1. The reference is only moved (lazy
+  // rescale) when some lane's sum exceeds 2^kLazyRescaleLog2 -- which bounds
+  // every probability by 2^8 without computing the block max -- or on the
+  // first block; then the block max is found, the output rescaled and the
+  // block recomputed from the K tile still in LDS.
+  auto scores_probs = [&](bf16x8 (&pf)[8]) -> float {
     const float mref = m_run == -__builtin_inff() ? 0.f : m_run;
-    float mx = -__builtin_inff();
+    float bsum = 0.f;
     f32x16 sa, sb;
-    // Scheduling fences keep each stage's operand loads next to its MFMAs
-    // (hoisting all of them would exceed the register budget).
     qk_tile(sa, 0);
     pipeline_reads<8, CALIBATT_READ_DEPTH, 0>();
     __builtin_amdgcn_sched_barrier(0);
     qk_tile(sb, 1);
-    probs_tile(sa, pf[0], pf[1], mref, mx);
+    probs_tile(sa, pf[0], pf[1], mref, bsum);
     pipeline_reads<8, CALIBATT_READ_DEPTH, 6>();
     __builtin_amdgcn_sched_barrier(0);
     qk_tile(sa, 2);
-    probs_tile(sb, pf[2], pf[3], mref, mx);
+    probs_tile(sb, pf[2], pf[3], mref, bsum);
     pipeline_reads<8, CALIBATT_READ_DEPTH, 6>();
     __builtin_amdgcn_sched_barrier(0);
     qk_tile(sb, 3);
-    probs_tile(sa, pf[4], pf[5], mref, mx);
+    probs_tile(sa, pf[4], pf[5], mref, bsum);
     pipeline_reads<8, CALIBATT_READ_DEPTH, 6>();
     __builtin_amdgcn_sched_barrier(0);
-    probs_tile(sb, pf[6], pf[7], mref, mx);
-    const float mblk = pair_max(mx) * sl;
-    const bool up = mblk > m_run + kLazyRescaleLog2;
-    if (__builtin_amdgcn_ballot_w64(up)) {
-      const float m_new = up ? mblk : m_run;
+    probs_tile(sb, pf[6], pf[7], mref, bsum);
+    const bool first = m_run == -__builtin_inff();
+    if (__builtin_amdgcn_ballot_w64(first || bsum > kLazyRescaleLimit)) {
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        qk_tile(sa, t);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(mx, sa[i]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const float m_new = __builtin_fmaxf(m_run, pair_max(mx) * sl);
       const float alpha = m_new == m_run ? 1.f : fast_exp2(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
       for (int u = 0; u < 4; ++u) oacc[u] *= alpha;
       m_run = m_new;
-      const float mref2 = m_run == -__builtin_inff() ? 0.f : m_run;
-      float unused = 0.f;
+      bsum = 0.f;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         qk_tile(sa, t);
-        probs_tile(sa, pf[2 * t], pf[2 * t + 1], mref2, unused);
+        probs_tile(sa, pf[2 * t], pf[2 * t + 1], m_run, bsum);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    return bsum;
   };
 
   for (int it = beg; it < end; ++it) {
@@ -322,8 +339,12 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const AttnArgs a)
     lds_barrier();
 
     bf16x8 pf[8];
-    scores_probs(pf);
-    if (key_lim < kBlock) zero_masked_probs(pf, key_lim);
+    float bsum = scores_probs(pf);
+    if (key_lim < kBlock) {
+      zero_masked_probs(pf, key_lim);
+      bsum = row_sum(pf);
+    }
+    l_run += bsum;
     lds_barrier();  // every wave is done with sK
     if (has_next) copy_tile<false>(ldsK, kh, cp, cnl * kBlock, N, wave, lane);
 
@@ -332,8 +353,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const AttnArgs a)
     else wait_vmem<0>();
     lds_barrier();
     pv_steps(pf, 0);
-    add_row_sum(pf);
-    pipeline_reads<16, CALIBATT_READ_DEPTH, 2>();
+    pipeline_reads<16, CALIBATT_READ_DEPTH, 0>();
     __builtin_amdgcn_sched_barrier(0);
     pv_steps(pf, 4);
     pipeline_reads<16, CALIBATT_READ_DEPTH, 0>();
