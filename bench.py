@@ -148,7 +148,7 @@ def calibration_case(cbs, draws: int):
         nnz = cbs.calibatt_finalize_mask(votes[t], draws, *w.rho, mask, off, idx)
         kept[t] = nnz / (w.heads * R * R)
     t_fin = (time.perf_counter() - t0) * 1e3
-    flop_energy = 2 * 2.0 * w.heads * (R * 128) ** 2 * w.head_dim   # two QK^T passes
+    flop_energy = 2.0 * w.heads * (R * 128) ** 2 * w.head_dim   # one Q K^T pass over every pair
     return {
         "workload": "calibration_480p", "heads": w.heads, "n_tokens": w.n_tokens, "draws": draws,
         "energy_ms_per_draw": round(t_energy / draws, 3),

@@ -239,8 +239,9 @@ int calibatt_sparse_attn_fwd(const void* q, const void* k, const void* v, void* 
 
 size_t calibatt_block_energy_workspace(int32_t heads, int32_t n_tokens) {
   if (heads <= 0 || n_tokens <= 0) return 0;
-  return (size_t)2 * sizeof(float) * (size_t)heads * (size_t)ceil_div(n_tokens, CALIBATT_BLOCK) *
-         CALIBATT_BLOCK;
+  const size_t R = (size_t)ceil_div(n_tokens, CALIBATT_BLOCK);
+  // per (head, key block, padded query row) and per (head, padded query row): two floats each
+  return (size_t)2 * sizeof(float) * (size_t)heads * R * CALIBATT_BLOCK * (R + 1);
 }
 
 int calibatt_block_energy(const void* q, const void* k, float* energy, int32_t heads,
@@ -264,15 +265,15 @@ int calibatt_block_energy(const void* q, const void* k, float* energy, int32_t h
   const size_t need = calibatt_block_energy_workspace(heads, n_tokens);
   if (!workspace || workspace_bytes < need)
     return fail(CALIBATT_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu", fn, workspace_bytes, need);
-  if (reinterpret_cast<uintptr_t>(workspace) & 3u)
-    return fail(CALIBATT_ERR_WORKSPACE, "%s: workspace must be 4-byte aligned", fn);
+  if (reinterpret_cast<uintptr_t>(workspace) & 7u)
+    return fail(CALIBATT_ERR_WORKSPACE, "%s: workspace must be 8-byte aligned", fn);
   EnergyArgs a;
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
   a.stride_head = stride_head;
   a.stride_token = stride_token;
-  a.row_max = static_cast<float*>(workspace);
-  a.row_sum = a.row_max + (size_t)heads * R * CALIBATT_BLOCK;
+  a.partials = static_cast<float*>(workspace);
+  a.row_stats = a.partials + (size_t)2 * heads * R * R * CALIBATT_BLOCK;
   a.energy = energy;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   a.n_tokens = n_tokens;

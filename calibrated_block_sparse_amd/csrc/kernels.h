@@ -47,8 +47,8 @@ struct EnergyArgs {
   const uint16_t* k;
   int64_t stride_head;
   int64_t stride_token;
-  float* row_max;            // [heads][R*128], log2 units
-  float* row_sum;            // [heads][R*128]
+  float* partials;           // float2 [heads][R][R*128]: (block partial sum, its reference)
+  float* row_stats;          // float2 [heads][R*128]: (final reference, row sum)
   float* energy;             // [heads][R][R]
   float scale_log2;
   int32_t n_tokens;

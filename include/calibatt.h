@@ -147,8 +147,10 @@ int calibatt_sparse_attn_fwd_vt(const void* q, const void* k, const void* vt, vo
                                 const calibatt_grid* grid, size_t vt_bytes, void* stream);
 
 /*
- * Bytes of device workspace calibatt_block_energy needs (row statistics:
- * two fp32 values per padded query row).
+ * Bytes of device workspace calibatt_block_energy needs: 8 * heads * R*128 *
+ * (R + 1) -- a (partial sum, reference) pair of fp32 per head, key block and
+ * padded query row, and a (reference, row sum) pair per head and padded
+ * query row (1.35 GB for 40 heads at N = 32760).
  */
 size_t calibatt_block_energy_workspace(int32_t heads, int32_t n_tokens);
 
@@ -161,7 +163,7 @@ size_t calibatt_block_energy_workspace(int32_t heads, int32_t n_tokens);
  *
  *   q, k       device bf16 [heads][N][128], strides as above
  *   energy     device fp32 [heads][R][R], output (dense, row-major)
- *   workspace  device, >= calibatt_block_energy_workspace(heads, N) bytes
+ *   workspace  device, 8-byte aligned, >= calibatt_block_energy_workspace(heads, N) bytes
  */
 int calibatt_block_energy(const void* q, const void* k, float* energy,
                           int32_t heads, int32_t n_tokens, int32_t head_dim,

@@ -96,7 +96,7 @@ def test_attention_argument_errors(lib):
 
 def test_energy_argument_errors(lib):
     ws = cbs.calibatt_block_energy_workspace(2, 1000)
-    assert ws == 2 * 4 * 2 * 8 * 128
+    assert ws == 2 * 4 * 2 * 8 * 128 * (8 + 1)
     f = lambda **kw: lib.calibatt_block_energy(kw.get("q", fake()), fake(), kw.get("e", fake()),
                                                2, kw.get("n", 1000), kw.get("d", 128), 1000 * 128,
                                                128, 0.1, kw.get("ws", fake()), kw.get("wsb", ws), None)
