@@ -78,12 +78,14 @@ def time_launches(fns, steps: int, warmup: int):
     return per, outer0.elapsed_time(outer1)
 
 
-def attn_case(cbs, name: str, steps: int, warmup: int, dense: bool = False):
+def attn_case(cbs, name: str, steps: int, warmup: int, dense: bool = False, mask=None,
+              tensors=None):
     from synth import ATTN_WORKLOADS, block_mask, qkv, repeat_flags
     w = ATTN_WORKLOADS[name]
-    q, k, v = qkv(w, device="cuda")
+    q, k, v = tensors if tensors is not None else qkv(w, device="cuda")
     o = torch.empty_like(q)
-    mask = np.ones((w.heads, w.n_blocks, w.n_blocks), np.uint8) if dense else block_mask(w)
+    if mask is None:
+        mask = np.ones((w.heads, w.n_blocks, w.n_blocks), np.uint8) if dense else block_mask(w)
     off, idx = cbs.compile_skiplist(torch.from_numpy(mask).cuda())
     flags = repeat_flags(w)
     grid = None
@@ -109,6 +111,57 @@ def attn_case(cbs, name: str, steps: int, warmup: int, dense: bool = False):
     per, total = time_launches([prepare, attend], steps, warmup)
     return dict(workload=w, pairs=pairs, per_ms=per.sum(axis=1), attn_ms=per[:, 1],
                 prep_ms=per[:, 0], total_ms=total, mask=mask, tensors=(q, k, v))
+
+
+SWEEP_FRACTIONS = (1.0, 0.75, 0.5, 0.375, 0.25, 0.125)
+
+
+def sweep_case(cbs, name: str, tensors, steps: int = 5, warmup: int = 2):
+    """Kept-fraction sweep at one shape: band + random masks at each kept
+    fraction, median step time of the attention kernel, and a least-squares
+    line of time against kept pairs (slope, intercept, R^2)."""
+    from synth import ATTN_WORKLOADS, mask_for_fraction
+    w = ATTN_WORKLOADS[name]
+    rows = []
+    for f in SWEEP_FRACTIONS:
+        mask = mask_for_fraction(w, f)
+        c = attn_case(cbs, name, steps, warmup, mask=mask, tensors=tensors)
+        ms = float(np.median(c["attn_ms"]))
+        rows.append((f, c["pairs"], ms))
+        del c
+    x = np.array([r[1] for r in rows], dtype=np.float64)
+    y = np.array([r[2] for r in rows], dtype=np.float64)
+    slope, icpt = np.polyfit(x, y, 1)
+    r2 = 1.0 - float(np.sum((y - (slope * x + icpt)) ** 2)) / float(np.sum((y - y.mean()) ** 2))
+    return {
+        "workload": name,
+        "kept_fraction": [r[0] for r in rows],
+        "pairs": [r[1] for r in rows],
+        "attn_ms": [round(r[2], 3) for r in rows],
+        "tflops": [round(r[1] * PAIR_FLOP / (r[2] * 1e-3) / 1e12, 1) for r in rows],
+        "fit_ms_per_million_pairs": round(slope * 1e6, 4),
+        "fit_intercept_ms": round(icpt, 4),
+        "fit_r2": round(r2, 6),
+    }
+
+
+def mfma_probe_case(cbs, iters: int = 20000, workgroups: int = 2048, reps: int = 3):
+    """Sustained matrix-core rate on this device (register-operand MFMA
+    loop), TFLOP/s: the median of `reps` timed launches after one warm-up."""
+    sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    cbs.calibatt_mfma_rate_probe(sink, iters, workgroups)
+    ts = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        flop = cbs.calibatt_mfma_rate_probe(sink, iters, workgroups)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ms = float(np.median(ts))
+    return flop / (ms * 1e-3) / 1e12, ms
 
 
 def calibration_case(cbs, draws: int):
@@ -212,6 +265,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calib-draws", type=int, default=4)
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-mask run")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the kept-fraction sweep")
     ap.add_argument("--copy-ref-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (counter reference)")
     args = ap.parse_args()
@@ -279,6 +333,13 @@ def main():
                      "kernel_ms_mean": round(per_launch_ms, 4), "kernel_hash": kernel_hash()},
         "v_transpose_ms_mean": round(float(np.mean(sp["prep_ms"])), 4),
     }
+    log("[bench] matrix-core rate probe")
+    onbox, probe_ms = mfma_probe_case(cbs)
+    out["roofline"]["onbox_mfma_loop_tflops"] = round(onbox, 1)
+    out["roofline"]["frac_of_onbox_mfma_loop"] = round(achieved / onbox, 4)
+    if not args.no_sweep:
+        log("[bench] kept-fraction sweep")
+        out["sweep"] = sweep_case(cbs, args.workload, sp["tensors"])
     if not args.no_extras:
         extras = {}
         for name in ("wan21_480p_layer", "mochi1_480p_layer"):

@@ -49,6 +49,7 @@ SIGNATURES = {
                                           _c.c_int32, _p, _p, _p, _p, _p]),
     "calibatt_compile_skiplist": (_c.c_int, [_p, _c.c_int32, _c.c_int32, _p, _p, _p, _p]),
     "calibatt_validate_skiplist": (_c.c_int, [_p, _p, _c.c_int64, _c.c_int32, _c.c_int32]),
+    "calibatt_mfma_rate_probe": (_c.c_int, [_p, _c.c_int64, _c.c_int32, _p]),
 }
 
 STATUS = {0: "OK", -1: "INVALID_ARG", -2: "UNSUPPORTED", -3: "BAD_SKIPLIST", -4: "WORKSPACE",
@@ -287,6 +288,16 @@ def calibatt_validate_skiplist(kv_offsets, kv_indices, heads: int, n_blocks_: in
                                                    idx.ctypes.data_as(ctypes.c_void_p),
                                                    idx.size, heads, n_blocks_)
     _check("calibatt_validate_skiplist", rc)
+
+
+def calibatt_mfma_rate_probe(sink, iters: int, workgroups: int, stream=None) -> int:
+    """Enqueue the matrix-core rate probe; returns the FLOP it performs
+    (workgroups * 4 waves * iters * 8 MFMAs * 32768)."""
+    if sink.dtype != torch.float32 or not sink.is_cuda or sink.numel() < 1:
+        raise ValueError("sink must be a CUDA float32 tensor with at least one element")
+    rc = load_library().calibatt_mfma_rate_probe(_ptr(sink), iters, workgroups, _stream(stream))
+    _check("calibatt_mfma_rate_probe", rc)
+    return int(workgroups) * 4 * int(iters) * 8 * 32768
 
 
 # ----------------------------------------------------------------------------

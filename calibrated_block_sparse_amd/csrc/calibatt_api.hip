@@ -63,7 +63,7 @@ extern "C" {
 
 const char* calibatt_last_error(void) { return g_last_error.c_str(); }
 
-int32_t calibatt_abi_version(void) { return 3; }
+int32_t calibatt_abi_version(void) { return 4; }
 
 
 size_t calibatt_sparse_attn_fwd_workspace(int32_t heads, int32_t n_tokens) {
@@ -388,6 +388,17 @@ int calibatt_validate_skiplist(const int32_t* kv_offsets, const int32_t* kv_indi
         return fail(CALIBATT_ERR_BAD_SKIPLIST, "%s: row %lld: indices not ascending", fn, (long long)r);
     }
   }
+  return ok();
+}
+
+int calibatt_mfma_rate_probe(float* sink, int64_t iters, int32_t workgroups, void* stream) {
+  if (!sink) return fail(CALIBATT_ERR_INVALID_ARG, "calibatt_mfma_rate_probe: sink is NULL");
+  if (iters < 0 || workgroups < 0)
+    return fail(CALIBATT_ERR_INVALID_ARG, "calibatt_mfma_rate_probe: iters (%lld) and workgroups (%d) must be >= 0",
+                (long long)iters, workgroups);
+  if (workgroups == 0) return ok();
+  const hipError_t e = launch_mfma_probe(sink, iters, workgroups, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "calibatt_mfma_rate_probe");
   return ok();
 }
 

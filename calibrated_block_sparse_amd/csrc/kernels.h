@@ -59,6 +59,7 @@ struct EnergyArgs {
 hipError_t launch_v_transpose(const VtArgs& a, hipStream_t stream);
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_block_energy(const EnergyArgs& a, hipStream_t stream);
+hipError_t launch_mfma_probe(float* sink, int64_t iters, int32_t workgroups, hipStream_t stream);
 
 hipError_t launch_select_votes(const float* energy, int32_t n_draws, int32_t heads,
                                int32_t n_blocks, uint64_t eps_fx, uint8_t* votes,

@@ -65,7 +65,8 @@ const char* calibatt_last_error(void);
 
 /* Interface version (increments on any change of this header). Version 2
  * added the workspace of calibatt_sparse_attn_fwd, version 3 its two halves
- * calibatt_prepare_vt and calibatt_sparse_attn_fwd_vt. */
+ * calibatt_prepare_vt and calibatt_sparse_attn_fwd_vt, version 4 the
+ * single-pass energy workspace and calibatt_mfma_rate_probe. */
 int32_t calibatt_abi_version(void);
 
 /*
@@ -150,7 +151,7 @@ int calibatt_sparse_attn_fwd_vt(const void* q, const void* k, const void* vt, vo
  * Bytes of device workspace calibatt_block_energy needs: 8 * heads * R*128 *
  * (R + 1) -- a (partial sum, reference) pair of fp32 per head, key block and
  * padded query row, and a (reference, row sum) pair per head and padded
- * query row (1.35 GB for 40 heads at N = 32760).
+ * query row (2.69 GB for 40 heads at N = 32760).
  */
 size_t calibatt_block_energy_workspace(int32_t heads, int32_t n_tokens);
 
@@ -240,6 +241,18 @@ int calibatt_compile_skiplist(const uint8_t* mask, int32_t heads, int32_t n_bloc
  */
 int calibatt_validate_skiplist(const int32_t* kv_offsets, const int32_t* kv_indices,
                                int64_t nnz, int32_t heads, int32_t n_blocks);
+
+/*
+ * Diagnostic, not part of the method: runs `workgroups` workgroups of four
+ * waves, each wave issuing iters x 8 independent bf16 32x32x16 MFMAs with
+ * register operands (32768 FLOP each), i.e.
+ *   workgroups * 4 * iters * 8 * 32768 FLOP,
+ * so that timing it on `stream` gives the matrix-core rate the device
+ * sustains under pure MFMA load. sink: device fp32[1], practically never
+ * written. Returns CALIBATT_ERR_INVALID_ARG for a NULL sink or negative
+ * sizes.
+ */
+int calibatt_mfma_rate_probe(float* sink, int64_t iters, int32_t workgroups, void* stream);
 
 #ifdef __cplusplus
 }

@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version(lib):
-    assert cbs.calibatt_abi_version() == 3
+    assert cbs.calibatt_abi_version() == 4
 
 
 def fake(n=16):
@@ -115,6 +115,13 @@ def test_mask_argument_errors(lib):
                                                        fake(), None, None)
     assert fin(0, 1, 2) == -1 and fin(256, 1, 2) == -1 and fin(64, 3, 2) == -1 and fin(64, 1, 0) == -1
     assert lib.calibatt_compile_skiplist(fake(), 40, 8000, fake(), fake(), None, None) == -2
+
+
+def test_mfma_probe_argument_errors(lib):
+    assert lib.calibatt_mfma_rate_probe(None, 10, 4, None) == -1
+    assert lib.calibatt_mfma_rate_probe(fake(), -1, 4, None) == -1
+    assert lib.calibatt_mfma_rate_probe(fake(), 10, -4, None) == -1
+    assert lib.calibatt_mfma_rate_probe(fake(), 10, 0, None) == 0   # nothing to launch
 
 
 def test_eps_fx_matches_oracle(lib):

@@ -221,3 +221,21 @@ def test_full_size_layer_sampled(gpu, name):
         e = assert_attn_close(got, want, f"{name} head {h}")
         if h % 10 == 0:
             say(f"  {name} head {h}: max-abs {e[0]:.2e} rel-fro {e[1]:.2e}")
+
+
+def test_mfma_rate_probe(gpu):
+    """The matrix-core probe runs through the C ABI and reports a rate
+    between a tenth of the published dense bf16 peak and that peak."""
+    sink = torch.zeros(1, dtype=torch.float32, device=DEV)
+    gpu.calibatt_mfma_rate_probe(sink, 100, 512)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    flop = gpu.calibatt_mfma_rate_probe(sink, 2000, 2048)
+    e1.record()
+    torch.cuda.synchronize()
+    assert flop == 2048 * 4 * 2000 * 8 * 32768
+    tflops = flop / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    say(f"  mfma probe: {tflops:.0f} TFLOP/s")
+    assert 251.7 < tflops < 2516.6 * 1.02
+    assert float(sink[0]) == 0.0
