@@ -49,11 +49,18 @@ SIGNATURES = {
                                           _c.c_int32, _p, _p, _p, _p, _p]),
     "calibatt_compile_skiplist": (_c.c_int, [_p, _c.c_int32, _c.c_int32, _p, _p, _p, _p]),
     "calibatt_validate_skiplist": (_c.c_int, [_p, _p, _c.c_int64, _c.c_int32, _c.c_int32]),
+    "calibatt_bank_write": (_c.c_int, [_c.c_char_p, _c.c_int32, _c.c_int32, _c.c_int32, _c.c_int32,
+                                       _p, _c.c_int32, _p, _p, _p, _p]),
+    "calibatt_bank_open": (_c.c_int, [_c.c_char_p, _p]),
+    "calibatt_bank_close": (None, [_p]),
+    "calibatt_bank_get_info": (_c.c_int, [_p, _p]),
+    "calibatt_bank_upload": (_c.c_int, [_p, _p, _c.c_size_t, _p]),
+    "calibatt_bank_lookup": (_c.c_int, [_p, _c.c_int32, _c.c_int32, _c.c_int32, _p]),
     "calibatt_mfma_rate_probe": (_c.c_int, [_p, _c.c_int64, _c.c_int32, _p]),
 }
 
 STATUS = {0: "OK", -1: "INVALID_ARG", -2: "UNSUPPORTED", -3: "BAD_SKIPLIST", -4: "WORKSPACE",
-          -5: "HIP"}
+          -5: "HIP", -6: "IO"}
 
 
 class CalibAttError(RuntimeError):
@@ -67,6 +74,21 @@ class Grid(ctypes.Structure):
     frame are computed by repeat heads."""
     _fields_ = [("frames", ctypes.c_int32), ("rows", ctypes.c_int32),
                 ("cols", ctypes.c_int32), ("anchors", ctypes.c_int32)]
+
+
+class BankInfo(ctypes.Structure):
+    """calibatt_bank_info."""
+    _fields_ = [("steps", ctypes.c_int32), ("layers", ctypes.c_int32), ("heads", ctypes.c_int32),
+                ("n_tokens", ctypes.c_int32), ("n_blocks", ctypes.c_int32),
+                ("n_entries", ctypes.c_int32), ("grid", Grid), ("total_nnz", ctypes.c_int64),
+                ("device_bytes", ctypes.c_size_t)]
+
+
+class BankEntry(ctypes.Structure):
+    """calibatt_bank_entry."""
+    _fields_ = [("entry", ctypes.c_int32), ("repeat_flags", ctypes.c_void_p),
+                ("kv_offsets", ctypes.c_void_p), ("kv_indices", ctypes.c_void_p),
+                ("nnz", ctypes.c_int64)]
 
 
 _lib = None

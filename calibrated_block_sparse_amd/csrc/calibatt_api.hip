@@ -14,11 +14,11 @@
 
 using namespace calibatt;
 
-namespace {
+namespace calibatt {
 
 thread_local std::string g_last_error;
 
-int fail(int code, const char* fmt, ...) {
+int api_fail(int code, const char* fmt, ...) {
   char buf[512];
   va_list ap;
   va_start(ap, fmt);
@@ -28,13 +28,17 @@ int fail(int code, const char* fmt, ...) {
   return code;
 }
 
-int ok() {
+int api_ok() {
   g_last_error.clear();
   return CALIBATT_OK;
 }
 
+}  // namespace calibatt
+
+namespace {
+
 int hip_fail(hipError_t e, const char* what) {
-  return fail(CALIBATT_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return api_fail(CALIBATT_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -45,13 +49,13 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int check_tensor_layout(const char* fn, int32_t heads, int32_t n_tokens, int32_t head_dim,
                         int64_t stride_head, int64_t stride_token) {
   if (heads < 0 || n_tokens < 0)
-    return fail(CALIBATT_ERR_INVALID_ARG, "%s: heads (%d) and n_tokens (%d) must be >= 0", fn,
+    return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: heads (%d) and n_tokens (%d) must be >= 0", fn,
                 heads, n_tokens);
   if (head_dim != CALIBATT_HEAD_DIM)
-    return fail(CALIBATT_ERR_UNSUPPORTED, "%s: head_dim %d unsupported (only %d)", fn, head_dim,
+    return api_fail(CALIBATT_ERR_UNSUPPORTED, "%s: head_dim %d unsupported (only %d)", fn, head_dim,
                 CALIBATT_HEAD_DIM);
   if (stride_token < head_dim || stride_head < 0 || stride_token % 8 || stride_head % 8)
-    return fail(CALIBATT_ERR_INVALID_ARG,
+    return api_fail(CALIBATT_ERR_INVALID_ARG,
                 "%s: strides (head %lld, token %lld) must be multiples of 8 with token >= %d", fn,
                 (long long)stride_head, (long long)stride_token, head_dim);
   return CALIBATT_OK;
@@ -61,9 +65,9 @@ int check_tensor_layout(const char* fn, int32_t heads, int32_t n_tokens, int32_t
 
 extern "C" {
 
-const char* calibatt_last_error(void) { return g_last_error.c_str(); }
+const char* calibatt_last_error(void) { return calibatt::g_last_error.c_str(); }
 
-int32_t calibatt_abi_version(void) { return 4; }
+int32_t calibatt_abi_version(void) { return 5; }
 
 
 size_t calibatt_sparse_attn_fwd_workspace(int32_t heads, int32_t n_tokens) {
@@ -78,15 +82,15 @@ static int attn_core(const char* fn, const void* q, const void* k, const void* v
                      int32_t heads, int32_t n_tokens, int64_t stride_head, int64_t stride_token,
                      float scale, const int32_t* kv_offsets, const int32_t* kv_indices, int64_t nnz,
                      const uint8_t* repeat_flags, const calibatt_grid* grid, hipStream_t stream) {
-  if (!q || !k || !o) return fail(CALIBATT_ERR_INVALID_ARG, "%s: null q/k/o", fn);
+  if (!q || !k || !o) return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: null q/k/o", fn);
   if (!aligned16(q) || !aligned16(k) || !aligned16(o))
-    return fail(CALIBATT_ERR_INVALID_ARG, "%s: q/k/o must be 16-byte aligned", fn);
+    return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: q/k/o must be 16-byte aligned", fn);
   if (!(scale > 0.f) || !std::isfinite(scale))
-    return fail(CALIBATT_ERR_INVALID_ARG, "%s: scale must be finite and > 0", fn);
-  if (nnz < 0) return fail(CALIBATT_ERR_INVALID_ARG, "%s: nnz < 0", fn);
+    return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: scale must be finite and > 0", fn);
+  if (nnz < 0) return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: nnz < 0", fn);
 
   const int32_t R = (int32_t)ceil_div(n_tokens, CALIBATT_BLOCK);
-  if ((int64_t)heads * R > 0x7fffffff) return fail(CALIBATT_ERR_UNSUPPORTED, "%s: too many tiles", fn);
+  if ((int64_t)heads * R > 0x7fffffff) return api_fail(CALIBATT_ERR_UNSUPPORTED, "%s: too many tiles", fn);
   std::vector<int32_t> rep_heads, sparse_heads;
   for (int32_t h = 0; h < heads; ++h)
     (repeat_flags && repeat_flags[h] ? rep_heads : sparse_heads).push_back(h);
@@ -94,13 +98,13 @@ static int attn_core(const char* fn, const void* q, const void* k, const void* v
   AttnArgs a;
   std::memset(&a, 0, sizeof a);
   if (!rep_heads.empty()) {
-    if (!grid) return fail(CALIBATT_ERR_INVALID_ARG, "%s: repeat heads need a grid", fn);
+    if (!grid) return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: repeat heads need a grid", fn);
     if (grid->frames <= 0 || grid->rows <= 0 || grid->cols <= 0 ||
         (int64_t)grid->frames * grid->rows * grid->cols != n_tokens)
-      return fail(CALIBATT_ERR_INVALID_ARG, "%s: grid %dx%dx%d does not cover N=%d", fn,
+      return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: grid %dx%dx%d does not cover N=%d", fn,
                   grid->frames, grid->rows, grid->cols, n_tokens);
     if (grid->anchors < 1 || grid->anchors > grid->rows)
-      return fail(CALIBATT_ERR_INVALID_ARG, "%s: anchors %d not in [1, rows=%d]", fn,
+      return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: anchors %d not in [1, rows=%d]", fn,
                   grid->anchors, grid->rows);
     a.frames = grid->frames;
     a.rows = grid->rows;
@@ -109,7 +113,7 @@ static int attn_core(const char* fn, const void* q, const void* k, const void* v
     a.anchor_queries = grid->frames * grid->anchors * grid->cols;
   }
   if (!sparse_heads.empty() && (!kv_offsets || (!kv_indices && nnz > 0)))
-    return fail(CALIBATT_ERR_INVALID_ARG, "%s: null kept-block list", fn);
+    return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: null kept-block list", fn);
 
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
@@ -135,21 +139,21 @@ static int attn_core(const char* fn, const void* q, const void* k, const void* v
     while (n < kMaxHeadsPerLaunch && ri < rep_heads.size()) { a.heads[n++] = rep_heads[ri++]; ++a.n_rep; }
     while (n < kMaxHeadsPerLaunch && si < sparse_heads.size()) { a.heads[n++] = sparse_heads[si++]; ++a.n_sparse; }
     const int64_t items = (int64_t)a.n_rep * a.rep_tiles + (int64_t)a.n_sparse * R;
-    if (items > 0x7fffffff) return fail(CALIBATT_ERR_UNSUPPORTED, "%s: too many tiles", fn);
+    if (items > 0x7fffffff) return api_fail(CALIBATT_ERR_UNSUPPORTED, "%s: too many tiles", fn);
     a.n_items = (int32_t)items;
     hipError_t e = launch_attn_fwd(a, stream);
     if (e != hipSuccess) return hip_fail(e, fn);
   }
-  return ok();
+  return api_ok();
 }
 
 static int check_workspace(const char* fn, int32_t heads, int32_t n_tokens, const void* ws,
                            size_t ws_bytes) {
   const size_t need = calibatt_sparse_attn_fwd_workspace(heads, n_tokens);
   if (!ws || ws_bytes < need)
-    return fail(CALIBATT_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu", fn, ws_bytes, need);
+    return api_fail(CALIBATT_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu", fn, ws_bytes, need);
   if (reinterpret_cast<uintptr_t>(ws) & 15u)
-    return fail(CALIBATT_ERR_WORKSPACE, "%s: workspace must be 16-byte aligned", fn);
+    return api_fail(CALIBATT_ERR_WORKSPACE, "%s: workspace must be 16-byte aligned", fn);
   return CALIBATT_OK;
 }
 
@@ -159,13 +163,13 @@ int calibatt_prepare_vt(const void* v, int32_t heads, int32_t n_tokens, int32_t 
   const char* fn = "calibatt_prepare_vt";
   int rc = check_tensor_layout(fn, heads, n_tokens, head_dim, stride_head, stride_token);
   if (rc) return rc;
-  if (heads == 0 || n_tokens == 0) return ok();
+  if (heads == 0 || n_tokens == 0) return api_ok();
   rc = check_workspace(fn, heads, n_tokens, workspace, workspace_bytes);
   if (rc) return rc;
-  if (!v) return fail(CALIBATT_ERR_INVALID_ARG, "%s: null v", fn);
-  if (!aligned16(v)) return fail(CALIBATT_ERR_INVALID_ARG, "%s: v must be 16-byte aligned", fn);
+  if (!v) return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: null v", fn);
+  if (!aligned16(v)) return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: v must be 16-byte aligned", fn);
   const int32_t R = (int32_t)ceil_div(n_tokens, CALIBATT_BLOCK);
-  if ((int64_t)heads * R > 0x7fffffff) return fail(CALIBATT_ERR_UNSUPPORTED, "%s: too many tiles", fn);
+  if ((int64_t)heads * R > 0x7fffffff) return api_fail(CALIBATT_ERR_UNSUPPORTED, "%s: too many tiles", fn);
   VtArgs t;
   t.v = static_cast<const uint16_t*>(v);
   t.vt = static_cast<uint16_t*>(workspace);
@@ -176,7 +180,7 @@ int calibatt_prepare_vt(const void* v, int32_t heads, int32_t n_tokens, int32_t 
   t.n_blocks = R;
   hipError_t e = launch_v_transpose(t, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, fn);
-  return ok();
+  return api_ok();
 }
 
 int calibatt_sparse_attn_fwd_vt(const void* q, const void* k, const void* vt, void* o,
@@ -188,7 +192,7 @@ int calibatt_sparse_attn_fwd_vt(const void* q, const void* k, const void* vt, vo
   const char* fn = "calibatt_sparse_attn_fwd_vt";
   int rc = check_tensor_layout(fn, heads, n_tokens, head_dim, stride_head, stride_token);
   if (rc) return rc;
-  if (heads == 0 || n_tokens == 0) return ok();
+  if (heads == 0 || n_tokens == 0) return api_ok();
   rc = check_workspace(fn, heads, n_tokens, vt, vt_bytes);
   if (rc) return rc;
   return attn_core(fn, q, k, vt, o, heads, n_tokens, stride_head, stride_token, scale, kv_offsets,
@@ -204,32 +208,32 @@ int calibatt_sparse_attn_fwd(const void* q, const void* k, const void* v, void* 
   const char* fn = "calibatt_sparse_attn_fwd";
   int rc = check_tensor_layout(fn, heads, n_tokens, head_dim, stride_head, stride_token);
   if (rc) return rc;
-  if (heads == 0 || n_tokens == 0) return ok();
+  if (heads == 0 || n_tokens == 0) return api_ok();
   rc = check_workspace(fn, heads, n_tokens, workspace, workspace_bytes);
   if (rc) return rc;
-  if (!v) return fail(CALIBATT_ERR_INVALID_ARG, "%s: null q/k/v/o", fn);
-  if (!aligned16(v)) return fail(CALIBATT_ERR_INVALID_ARG, "%s: q/k/v/o must be 16-byte aligned", fn);
+  if (!v) return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: null q/k/v/o", fn);
+  if (!aligned16(v)) return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: q/k/v/o must be 16-byte aligned", fn);
   // validate everything the attention needs before enqueuing the pre-pass
-  if (!q || !k || !o) return fail(CALIBATT_ERR_INVALID_ARG, "%s: null q/k/v/o", fn);
+  if (!q || !k || !o) return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: null q/k/v/o", fn);
   if (!aligned16(q) || !aligned16(k) || !aligned16(o))
-    return fail(CALIBATT_ERR_INVALID_ARG, "%s: q/k/v/o must be 16-byte aligned", fn);
+    return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: q/k/v/o must be 16-byte aligned", fn);
   if (!(scale > 0.f) || !std::isfinite(scale))
-    return fail(CALIBATT_ERR_INVALID_ARG, "%s: scale must be finite and > 0", fn);
-  if (nnz < 0) return fail(CALIBATT_ERR_INVALID_ARG, "%s: nnz < 0", fn);
+    return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: scale must be finite and > 0", fn);
+  if (nnz < 0) return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: nnz < 0", fn);
   bool any_rep = false, any_sparse = false;
   for (int32_t h = 0; h < heads; ++h) (repeat_flags && repeat_flags[h] ? any_rep : any_sparse) = true;
   if (any_rep) {
-    if (!grid) return fail(CALIBATT_ERR_INVALID_ARG, "%s: repeat heads need a grid", fn);
+    if (!grid) return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: repeat heads need a grid", fn);
     if (grid->frames <= 0 || grid->rows <= 0 || grid->cols <= 0 ||
         (int64_t)grid->frames * grid->rows * grid->cols != n_tokens)
-      return fail(CALIBATT_ERR_INVALID_ARG, "%s: grid %dx%dx%d does not cover N=%d", fn,
+      return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: grid %dx%dx%d does not cover N=%d", fn,
                   grid->frames, grid->rows, grid->cols, n_tokens);
     if (grid->anchors < 1 || grid->anchors > grid->rows)
-      return fail(CALIBATT_ERR_INVALID_ARG, "%s: anchors %d not in [1, rows=%d]", fn,
+      return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: anchors %d not in [1, rows=%d]", fn,
                   grid->anchors, grid->rows);
   }
   if (any_sparse && (!kv_offsets || (!kv_indices && nnz > 0)))
-    return fail(CALIBATT_ERR_INVALID_ARG, "%s: null kept-block list", fn);
+    return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: null kept-block list", fn);
   rc = calibatt_prepare_vt(v, heads, n_tokens, head_dim, stride_head, stride_token, workspace,
                            workspace_bytes, stream);
   if (rc) return rc;
@@ -251,22 +255,22 @@ int calibatt_block_energy(const void* q, const void* k, float* energy, int32_t h
   const char* fn = "calibatt_block_energy";
   int rc = check_tensor_layout(fn, heads, n_tokens, head_dim, stride_head, stride_token);
   if (rc) return rc;
-  if (heads == 0 || n_tokens == 0) return ok();
-  if (!q || !k || !energy) return fail(CALIBATT_ERR_INVALID_ARG, "%s: null q/k/energy", fn);
+  if (heads == 0 || n_tokens == 0) return api_ok();
+  if (!q || !k || !energy) return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: null q/k/energy", fn);
   if (!aligned16(q) || !aligned16(k))
-    return fail(CALIBATT_ERR_INVALID_ARG, "%s: q/k must be 16-byte aligned", fn);
+    return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: q/k must be 16-byte aligned", fn);
   if (!(scale > 0.f) || !std::isfinite(scale))
-    return fail(CALIBATT_ERR_INVALID_ARG, "%s: scale must be finite and > 0", fn);
+    return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: scale must be finite and > 0", fn);
   const int64_t R = ceil_div(n_tokens, CALIBATT_BLOCK);
   if (R > CALIBATT_MAX_BLOCKS)
-    return fail(CALIBATT_ERR_UNSUPPORTED, "%s: %lld blocks > %d", fn, (long long)R,
+    return api_fail(CALIBATT_ERR_UNSUPPORTED, "%s: %lld blocks > %d", fn, (long long)R,
                 CALIBATT_MAX_BLOCKS);
-  if ((int64_t)heads * R > 0x7fffffff) return fail(CALIBATT_ERR_UNSUPPORTED, "%s: too many tiles", fn);
+  if ((int64_t)heads * R > 0x7fffffff) return api_fail(CALIBATT_ERR_UNSUPPORTED, "%s: too many tiles", fn);
   const size_t need = calibatt_block_energy_workspace(heads, n_tokens);
   if (!workspace || workspace_bytes < need)
-    return fail(CALIBATT_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu", fn, workspace_bytes, need);
+    return api_fail(CALIBATT_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu", fn, workspace_bytes, need);
   if (reinterpret_cast<uintptr_t>(workspace) & 7u)
-    return fail(CALIBATT_ERR_WORKSPACE, "%s: workspace must be 8-byte aligned", fn);
+    return api_fail(CALIBATT_ERR_WORKSPACE, "%s: workspace must be 8-byte aligned", fn);
   EnergyArgs a;
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
@@ -281,7 +285,7 @@ int calibatt_block_energy(const void* q, const void* k, float* energy, int32_t h
   a.heads = heads;
   hipError_t e = launch_block_energy(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, fn);
-  return ok();
+  return api_ok();
 }
 
 uint64_t calibatt_eps_fx(double t, double T, double A, double C, double k) {
@@ -296,27 +300,27 @@ int calibatt_build_mask(const float* energy, int32_t n_draws, int32_t heads, int
                         uint64_t eps_fx, uint8_t* votes, int32_t* n_sel, void* stream) {
   const char* fn = "calibatt_build_mask";
   if (n_draws < 0 || heads < 0 || n_blocks < 0)
-    return fail(CALIBATT_ERR_INVALID_ARG, "%s: negative size", fn);
-  if (n_draws == 0 || heads == 0 || n_blocks == 0) return ok();
+    return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: negative size", fn);
+  if (n_draws == 0 || heads == 0 || n_blocks == 0) return api_ok();
   if (n_blocks > CALIBATT_MAX_BLOCKS)
-    return fail(CALIBATT_ERR_UNSUPPORTED, "%s: %d blocks > %d", fn, n_blocks, CALIBATT_MAX_BLOCKS);
-  if (!energy || !votes) return fail(CALIBATT_ERR_INVALID_ARG, "%s: null energy/votes", fn);
-  if ((int64_t)heads * n_blocks > 0x7fffffff) return fail(CALIBATT_ERR_UNSUPPORTED, "%s: too many rows", fn);
+    return api_fail(CALIBATT_ERR_UNSUPPORTED, "%s: %d blocks > %d", fn, n_blocks, CALIBATT_MAX_BLOCKS);
+  if (!energy || !votes) return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: null energy/votes", fn);
+  if ((int64_t)heads * n_blocks > 0x7fffffff) return api_fail(CALIBATT_ERR_UNSUPPORTED, "%s: too many rows", fn);
   hipError_t e = launch_select_votes(energy, n_draws, heads, n_blocks, eps_fx, votes, n_sel,
                                      static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, fn);
-  return ok();
+  return api_ok();
 }
 
 static int compile_common(const char* fn, const uint8_t* src, int mode, int32_t heads,
                           int32_t n_blocks, int32_t n_prompts, int32_t rho_num, int32_t rho_den,
                           uint8_t* mask, int32_t* kv_offsets, int32_t* kv_indices,
                           int64_t* nnz_out, void* stream) {
-  if (heads < 0 || n_blocks < 0) return fail(CALIBATT_ERR_INVALID_ARG, "%s: negative size", fn);
+  if (heads < 0 || n_blocks < 0) return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: negative size", fn);
   const int64_t rows = (int64_t)heads * n_blocks;
   if (rows * n_blocks >= 0x7fffffffLL)
-    return fail(CALIBATT_ERR_UNSUPPORTED, "%s: heads*R*R must be < 2^31", fn);
-  if (!kv_offsets) return fail(CALIBATT_ERR_INVALID_ARG, "%s: null kv_offsets", fn);
+    return api_fail(CALIBATT_ERR_UNSUPPORTED, "%s: heads*R*R must be < 2^31", fn);
+  if (!kv_offsets) return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: null kv_offsets", fn);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (rows == 0) {
@@ -324,7 +328,7 @@ static int compile_common(const char* fn, const uint8_t* src, int mode, int32_t 
     if (e != hipSuccess) return hip_fail(e, fn);
   } else {
     if (!src || !kv_indices || (mode == 1 && !mask))
-      return fail(CALIBATT_ERR_INVALID_ARG, "%s: null input/output", fn);
+      return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: null input/output", fn);
     e = launch_row_counts(src, (int32_t)rows, n_blocks, mode, n_prompts, rho_num, rho_den, mask,
                           kv_offsets, s);
     if (e == hipSuccess) e = launch_offsets_scan(kv_offsets, (int32_t)rows, s);
@@ -339,7 +343,7 @@ static int compile_common(const char* fn, const uint8_t* src, int mode, int32_t 
     if (e != hipSuccess) return hip_fail(e, fn);
     *nnz_out = nnz;
   }
-  return ok();
+  return api_ok();
 }
 
 int calibatt_finalize_mask(const uint8_t* votes, int32_t heads, int32_t n_blocks,
@@ -348,9 +352,9 @@ int calibatt_finalize_mask(const uint8_t* votes, int32_t heads, int32_t n_blocks
                            void* stream) {
   const char* fn = "calibatt_finalize_mask";
   if (n_prompts < 1 || n_prompts > 255)
-    return fail(CALIBATT_ERR_INVALID_ARG, "%s: n_prompts %d not in [1, 255]", fn, n_prompts);
+    return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: n_prompts %d not in [1, 255]", fn, n_prompts);
   if (rho_den < 1 || rho_num < 0 || rho_num > rho_den || rho_den > (1 << 20))
-    return fail(CALIBATT_ERR_INVALID_ARG, "%s: rho %d/%d invalid", fn, rho_num, rho_den);
+    return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: rho %d/%d invalid", fn, rho_num, rho_den);
   return compile_common(fn, votes, 1, heads, n_blocks, n_prompts, rho_num, rho_den, mask,
                         kv_offsets, kv_indices, nnz_out, stream);
 }
@@ -366,40 +370,40 @@ int calibatt_validate_skiplist(const int32_t* kv_offsets, const int32_t* kv_indi
                                int32_t heads, int32_t n_blocks) {
   const char* fn = "calibatt_validate_skiplist";
   if (heads < 0 || n_blocks < 0 || nnz < 0)
-    return fail(CALIBATT_ERR_INVALID_ARG, "%s: negative size", fn);
+    return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: negative size", fn);
   if (!kv_offsets || (nnz > 0 && !kv_indices))
-    return fail(CALIBATT_ERR_INVALID_ARG, "%s: null pointer", fn);
+    return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: null pointer", fn);
   const int64_t rows = (int64_t)heads * n_blocks;
-  if (kv_offsets[0] != 0) return fail(CALIBATT_ERR_BAD_SKIPLIST, "%s: offsets[0] = %d", fn, kv_offsets[0]);
+  if (kv_offsets[0] != 0) return api_fail(CALIBATT_ERR_BAD_SKIPLIST, "%s: offsets[0] = %d", fn, kv_offsets[0]);
   if (kv_offsets[rows] != nnz)
-    return fail(CALIBATT_ERR_BAD_SKIPLIST, "%s: offsets[%lld] = %d != nnz %lld", fn,
+    return api_fail(CALIBATT_ERR_BAD_SKIPLIST, "%s: offsets[%lld] = %d != nnz %lld", fn,
                 (long long)rows, kv_offsets[rows], (long long)nnz);
   for (int64_t r = 0; r < rows; ++r) {
     const int32_t b = kv_offsets[r], e = kv_offsets[r + 1];
-    if (e < b) return fail(CALIBATT_ERR_BAD_SKIPLIST, "%s: row %lld: offsets decrease", fn, (long long)r);
+    if (e < b) return api_fail(CALIBATT_ERR_BAD_SKIPLIST, "%s: row %lld: offsets decrease", fn, (long long)r);
     if (e - b > n_blocks)
-      return fail(CALIBATT_ERR_BAD_SKIPLIST, "%s: row %lld: %d entries > R", fn, (long long)r, e - b);
+      return api_fail(CALIBATT_ERR_BAD_SKIPLIST, "%s: row %lld: %d entries > R", fn, (long long)r, e - b);
     for (int32_t i = b; i < e; ++i) {
       const int32_t c = kv_indices[i];
       if (c < 0 || c >= n_blocks)
-        return fail(CALIBATT_ERR_BAD_SKIPLIST, "%s: row %lld: index %d out of [0, %d)", fn,
+        return api_fail(CALIBATT_ERR_BAD_SKIPLIST, "%s: row %lld: index %d out of [0, %d)", fn,
                     (long long)r, c, n_blocks);
       if (i > b && c <= kv_indices[i - 1])
-        return fail(CALIBATT_ERR_BAD_SKIPLIST, "%s: row %lld: indices not ascending", fn, (long long)r);
+        return api_fail(CALIBATT_ERR_BAD_SKIPLIST, "%s: row %lld: indices not ascending", fn, (long long)r);
     }
   }
-  return ok();
+  return api_ok();
 }
 
 int calibatt_mfma_rate_probe(float* sink, int64_t iters, int32_t workgroups, void* stream) {
-  if (!sink) return fail(CALIBATT_ERR_INVALID_ARG, "calibatt_mfma_rate_probe: sink is NULL");
+  if (!sink) return api_fail(CALIBATT_ERR_INVALID_ARG, "calibatt_mfma_rate_probe: sink is NULL");
   if (iters < 0 || workgroups < 0)
-    return fail(CALIBATT_ERR_INVALID_ARG, "calibatt_mfma_rate_probe: iters (%lld) and workgroups (%d) must be >= 0",
+    return api_fail(CALIBATT_ERR_INVALID_ARG, "calibatt_mfma_rate_probe: iters (%lld) and workgroups (%d) must be >= 0",
                 (long long)iters, workgroups);
-  if (workgroups == 0) return ok();
+  if (workgroups == 0) return api_ok();
   const hipError_t e = launch_mfma_probe(sink, iters, workgroups, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "calibatt_mfma_rate_probe");
-  return ok();
+  return api_ok();
 }
 
 }  // extern "C"

@@ -56,6 +56,10 @@ struct EnergyArgs {
   int32_t heads;
 };
 
+// Error reporting of the C ABI (thread-local message, returned status).
+int api_fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int api_ok();
+
 hipError_t launch_v_transpose(const VtArgs& a, hipStream_t stream);
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_block_energy(const EnergyArgs& a, hipStream_t stream);

@@ -19,8 +19,9 @@
  *   contiguous. Base pointers must be 16-byte aligned and both strides
  *   multiples of 8 elements. Batch is folded into heads.
  * - Every pointer named "device" is device memory owned by the caller. The
- *   library allocates nothing and keeps no state between calls except the
- *   thread-local error string.
+ *   library allocates no device memory and keeps no state between calls
+ *   except the thread-local error string and the host memory of a mask bank
+ *   handle (calibatt_bank_open .. calibatt_bank_close).
  * - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
  *   and is asynchronous unless an entry point says otherwise. Argument
  *   errors are reported before anything is enqueued; launch failures return
@@ -43,7 +44,8 @@ enum {
   CALIBATT_ERR_UNSUPPORTED = -2,  /* D != 128, sizes beyond the limits below */
   CALIBATT_ERR_BAD_SKIPLIST = -3, /* malformed kept-block list (validators) */
   CALIBATT_ERR_WORKSPACE = -4,    /* workspace missing or too small */
-  CALIBATT_ERR_HIP = -5           /* a HIP runtime call or launch failed */
+  CALIBATT_ERR_HIP = -5,          /* a HIP runtime call or launch failed */
+  CALIBATT_ERR_IO = -6            /* mask bank file missing, unreadable or corrupt */
 };
 
 #define CALIBATT_BLOCK 128
@@ -66,7 +68,8 @@ const char* calibatt_last_error(void);
 /* Interface version (increments on any change of this header). Version 2
  * added the workspace of calibatt_sparse_attn_fwd, version 3 its two halves
  * calibatt_prepare_vt and calibatt_sparse_attn_fwd_vt, version 4 the
- * single-pass energy workspace and calibatt_mfma_rate_probe. */
+ * single-pass energy workspace and calibatt_mfma_rate_probe, version 5 the
+ * mask bank (calibatt_bank_*) and CALIBATT_ERR_IO. */
 int32_t calibatt_abi_version(void);
 
 /*
@@ -241,6 +244,91 @@ int calibatt_compile_skiplist(const uint8_t* mask, int32_t heads, int32_t n_bloc
  */
 int calibatt_validate_skiplist(const int32_t* kv_offsets, const int32_t* kv_indices,
                                int64_t nnz, int32_t heads, int32_t n_blocks);
+
+/*
+ * Mask bank ([CalibAtt blog] §一: calibration compiles one static mask per
+ * (timestep, layer, head); §三 online inference: each attention call fetches
+ * the kept-block list or repeat flag of its (t, l, h) from a table, making
+ * no decision at run time). A bank holds, for T timesteps x L layers, the
+ * index of an entry; an entry is what one attention call over H heads needs:
+ * repeat flags and kept-block lists (CSR as for calibatt_sparse_attn_fwd).
+ * Several (t, l) may share an entry.
+ *
+ * File layout (little-endian, version 1):
+ *   [0, 128)      header: char magic[8] = "CBSMBNK1"; u32 version = 1;
+ *                 u32 header bytes = 128; i32 steps T, layers L, heads H,
+ *                 n_tokens N, n_blocks R = ceil(N/128), frames, rows, cols,
+ *                 anchors (all four 0 when the bank has no grid),
+ *                 n_entries E; i64 table offset; i64 file bytes;
+ *                 u64 FNV-1a-64 of bytes [128, file bytes); zeros to 128.
+ *   [128, ...)    i32 entry[T][L]
+ *   table         E x { i64 payload offset, i64 nnz, u64 FNV-1a-64 of the payload }
+ *   payloads      each at a multiple of 256 bytes: u8 repeat_flags[H]
+ *                 (0/1), zeros to a multiple of 4, i32 kv_offsets[H*R + 1],
+ *                 i32 kv_indices[nnz]; zeros to the next 256 bytes.
+ * The file ends at the end of the last padded payload.
+ */
+typedef struct calibatt_bank calibatt_bank; /* opaque host object */
+
+typedef struct calibatt_bank_info {
+  int32_t steps, layers, heads, n_tokens, n_blocks, n_entries;
+  calibatt_grid grid;   /* all zero when the bank has no grid */
+  int64_t total_nnz;    /* sum of nnz over entries */
+  size_t device_bytes;  /* size of the buffer calibatt_bank_upload needs */
+} calibatt_bank_info;
+
+typedef struct calibatt_bank_entry {
+  int32_t entry;               /* entry index */
+  const uint8_t* repeat_flags; /* host, [H]; valid until calibatt_bank_close */
+  const int32_t* kv_offsets;   /* [H*R + 1], host or device (see lookup) */
+  const int32_t* kv_indices;   /* [nnz] */
+  int64_t nnz;
+} calibatt_bank_entry;
+
+/*
+ * Write a bank file (synchronous host I/O; written to path + ".tmp" and
+ * renamed over path). entry_of: host int32 [steps*layers], values in
+ * [0, n_entries). Per entry e (host arrays): repeat_flags[e] uint8 [heads]
+ * or NULL (no repeat head; repeat_flags itself may be NULL), kv_offsets[e]
+ * int32 [heads*R + 1], kv_indices[e] int32 [kv_offsets[e][heads*R]]. Lists
+ * must pass calibatt_validate_skiplist (else CALIBATT_ERR_BAD_SKIPLIST);
+ * flags must be 0/1, and any repeat flag needs a grid covering n_tokens.
+ * I/O failures give CALIBATT_ERR_IO.
+ */
+int calibatt_bank_write(const char* path, int32_t steps, int32_t layers, int32_t heads,
+                        int32_t n_tokens, const calibatt_grid* grid, int32_t n_entries,
+                        const int32_t* entry_of, const uint8_t* const* repeat_flags,
+                        const int32_t* const* kv_offsets, const int32_t* const* kv_indices);
+
+/*
+ * Read and check a bank file (magic, version, sizes, both checksums, every
+ * list and flag); on success *out is a new handle owning the file's bytes in
+ * host memory. Corrupt or unreadable files give CALIBATT_ERR_IO, malformed
+ * lists CALIBATT_ERR_BAD_SKIPLIST; *out is then NULL.
+ */
+int calibatt_bank_open(const char* path, calibatt_bank** out);
+
+/* Free a handle (NULL is ignored). Device buffers it was uploaded to stay the caller's. */
+void calibatt_bank_close(calibatt_bank* bank);
+
+int calibatt_bank_get_info(const calibatt_bank* bank, calibatt_bank_info* out);
+
+/*
+ * Copy every entry's lists into `device` (caller-owned, 256-byte aligned, at
+ * least info.device_bytes) with an asynchronous copy on `stream`, and
+ * remember it for lookups with on_device = 1. The buffer must outlive those
+ * lookups' use; uploading again rebinds the handle to the new buffer.
+ */
+int calibatt_bank_upload(calibatt_bank* bank, void* device, size_t bytes, void* stream);
+
+/*
+ * The entry of timestep t and layer l: O(1), no I/O, no device work.
+ * on_device = 0 returns host pointers into the handle; 1 returns pointers
+ * into the uploaded buffer (CALIBATT_ERR_INVALID_ARG if none). repeat_flags
+ * is always host memory, as calibatt_sparse_attn_fwd takes it.
+ */
+int calibatt_bank_lookup(const calibatt_bank* bank, int32_t t, int32_t l, int32_t on_device,
+                         calibatt_bank_entry* out);
 
 /*
  * Diagnostic, not part of the method: runs `workgroups` workgroups of four

@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version(lib):
-    assert cbs.calibatt_abi_version() == 4
+    assert cbs.calibatt_abi_version() == 5
 
 
 def fake(n=16):
