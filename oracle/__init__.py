@@ -17,7 +17,10 @@ Floating point is fp64 throughout; bf16 inputs are decoded exactly.
 Pins (what ties each function to something other than itself) live in
 tests/test_oracle_*.py. One function is not pinned to anything independent:
 the selection on energies that come from attention rather than from a given
-array is only as good as its two pinned halves (energy, selection).
+array is only as good as its two pinned halves (energy, selection). The
+spatial similarity score is PARITY UNPINNED as to its formula (the pages
+give none; calibration.py states the reading taken), and pinned to that
+reading by closed forms.
 """
 
 from .attention import (  # noqa: F401
@@ -29,4 +32,5 @@ from .calibration import (  # noqa: F401
     FX_BITS, block_energy_row, block_energy, quantize_energy, eps_schedule,
     eps_fx, greedy_select_row, greedy_select, accumulate_votes, binarize,
     compile_skiplist, skiplist_to_mask,
+    GAMMA, row_profiles, spatial_similarity, classify_repeat,
 )

@@ -154,3 +154,63 @@ def pairs_flop(n_pairs: int, head_dim: int = 128) -> float:
 
 
 __all__ = [n for n in dir() if not n.startswith("_") and n not in ("math", "np")]
+
+
+# ----------------------------------------------------------------------------
+# Spatial similarity of a head and its repeat classification ([CalibAtt
+# blog] §二 observation 4: rows of one frame attend alike; §三: a spatial
+# similarity score s per (t, l, h), above gamma = 0.87 the head is computed
+# from k anchor rows and broadcast). The pages give no formula for s. The
+# reading taken here, with the anchors of repeat_head_attention:
+#
+# * profile of spatial row (f, y): the mean over its W query tokens of the
+#   post-softmax attention summed per key block (block granularity, as the
+#   masks), rho_{f,y}[c] = (1/W) sum_{i in row (f,y)} sum_{j in J_c} P_ij;
+# * s = mean over frames f and non-anchor rows y of the cosine similarity
+#   between rho_{f,y} and the profile of its anchor row, rho_{f,a(y)}
+#   (1 when every row is an anchor); averaged over prompts by the caller;
+# * repeat iff s > gamma ("exceeds").
+# PARITY UNPINNED as to the formula (the pages have none); the function is
+# pinned to its reading by closed forms in tests/test_oracle_calibration.py.
+
+GAMMA = 0.87
+
+
+def row_profiles(q, k, scale: float, frames: int, rows: int, cols: int) -> np.ndarray:
+    """rho: [frames*rows][R], one row per spatial row (f, y)."""
+    q, k = as_f64(q), as_f64(k)
+    N = q.shape[0]
+    assert frames * rows * cols == N
+    R = (N + BLOCK - 1) // BLOCK
+    out = np.zeros((frames * rows, R))
+    for fy in range(frames * rows):
+        qi = q[fy * cols:(fy + 1) * cols]
+        s = (qi @ k.T) * scale
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        for c in range(R):
+            out[fy, c] = p[:, c * BLOCK:min((c + 1) * BLOCK, N)].sum() / cols
+    return out
+
+
+def spatial_similarity(q, k, scale: float, frames: int, rows: int, cols: int,
+                       anchors: int) -> float:
+    """s of one head for one prompt (see the reading above)."""
+    from .attention import anchor_of_row
+    prof = row_profiles(q, k, scale, frames, rows, cols)
+    a = anchor_of_row(rows, anchors)
+    total, count = 0.0, 0
+    for f in range(frames):
+        for y in range(rows):
+            if a[y] == y:
+                continue
+            u = prof[f * rows + y]
+            w = prof[f * rows + a[y]]
+            total += float(u @ w) / (np.linalg.norm(u) * np.linalg.norm(w))
+            count += 1
+    return 1.0 if count == 0 else total / count
+
+
+def classify_repeat(s_mean, gamma: float = GAMMA) -> np.ndarray:
+    """Repeat flags (uint8) of heads whose prompt-averaged s exceeds gamma."""
+    return (np.asarray(s_mean, dtype=np.float64) > gamma).astype(np.uint8)

@@ -239,3 +239,80 @@ def test_compile_roundtrip():
     assert np.array_equal(oracle.skiplist_to_mask(off, idx, 3, 37), m)
     for row in range(3 * 37):
         assert np.all(np.diff(idx[off[row]:off[row + 1]]) > 0)
+
+
+# ----------------------------------------------------------------------------
+# Spatial similarity (reading of [CalibAtt blog] §二 observation 4 / §三; the
+# pages give no formula, so these pins tie the oracle to the stated reading).
+
+
+def _onehot_case(pattern):
+    """frames 1 x rows 8 x cols 32 (N = 256, two key blocks): every query of
+    spatial row y points along unit direction e_{pattern[y]} with length 64,
+    keys of block b are e_b, scale 1, so row y attends to block pattern[y]
+    up to e^-64 and its profile is that one-hot vector."""
+    F, Hs, W = 1, 8, 32
+    N = F * Hs * W
+    k = np.zeros((N, 128))
+    k[:128, 0] = 1.0
+    k[128:, 1] = 1.0
+    q = np.zeros((N, 128))
+    for y in range(Hs):
+        q[y * W:(y + 1) * W, pattern[y]] = 64.0
+    return q, k, (F, Hs, W)
+
+
+def test_spatial_similarity_onehot_closed_form():
+    # anchors 2 of 8 rows: A(m) = floor((2m+1)*8/4) = {2, 6}; rows 0-3 -> 2, 4-7 -> 6.
+    # non-anchor rows 0,1,3,4,5,7 agree with their anchor's block in 4 cases.
+    pattern = [0, 0, 0, 1, 1, 0, 1, 1]
+    q, k, (F, Hs, W) = _onehot_case(pattern)
+    assert list(oracle.anchor_rows(Hs, 2)) == [2, 6]
+    prof = oracle.row_profiles(q, k, 1.0, F, Hs, W)
+    np.testing.assert_allclose(prof, np.eye(2)[pattern], atol=1e-12)
+    s = oracle.spatial_similarity(q, k, 1.0, F, Hs, W, 2)
+    assert abs(s - 4 / 6) < 1e-12
+
+
+def test_spatial_similarity_zero_queries_is_one():
+    F, Hs, W = 2, 5, 40                       # N = 400, R = 4, last block 16 keys
+    k = np.random.default_rng(3).standard_normal((F * Hs * W, 128))
+    q = np.zeros_like(k)
+    prof = oracle.row_profiles(q, k, 0.1, F, Hs, W)
+    np.testing.assert_allclose(prof, np.broadcast_to(np.array([128, 128, 128, 16]) / 400, prof.shape),
+                               atol=1e-15)
+    assert abs(oracle.spatial_similarity(q, k, 0.1, F, Hs, W, 2) - 1.0) < 1e-12
+
+
+def test_spatial_similarity_rows_alike_within_frames_is_one():
+    F, Hs, W = 2, 6, 24
+    rng = np.random.default_rng(4)
+    k = rng.standard_normal((F * Hs * W, 128))
+    base = rng.standard_normal((F, 1, W, 128))
+    q = np.broadcast_to(base, (F, Hs, W, 128)).reshape(-1, 128)
+    assert abs(oracle.spatial_similarity(q, k, 0.2, F, Hs, W, 3) - 1.0) < 1e-12
+
+
+def test_spatial_similarity_every_row_an_anchor():
+    F, Hs, W = 1, 4, 32
+    rng = np.random.default_rng(5)
+    q, k = rng.standard_normal((2, F * Hs * W, 128))
+    assert list(oracle.anchor_of_row(Hs, Hs)) == list(range(Hs))
+    assert oracle.spatial_similarity(q, k, 0.1, F, Hs, W, Hs) == 1.0
+
+
+def test_spatial_similarity_bounds_and_profile_sums():
+    F, Hs, W = 2, 6, 30
+    rng = np.random.default_rng(6)
+    q, k = rng.standard_normal((2, F * Hs * W, 128)) * 1.5
+    prof = oracle.row_profiles(q, k, 0.3, F, Hs, W)
+    np.testing.assert_allclose(prof.sum(axis=1), 1.0, atol=1e-12)
+    assert (prof >= 0).all()
+    s = oracle.spatial_similarity(q, k, 0.3, F, Hs, W, 2)
+    assert 0.0 < s < 1.0
+
+
+def test_classify_repeat_is_strictly_above_gamma():
+    assert oracle.GAMMA == 0.87
+    got = oracle.classify_repeat([0.86, 0.87, np.nextafter(0.87, 1.0), 0.99])
+    assert got.tolist() == [0, 0, 1, 1] and got.dtype == np.uint8
