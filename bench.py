@@ -178,20 +178,29 @@ def calibration_case(cbs, draws: int):
     votes = {t: torch.zeros(w.heads, R, R, dtype=torch.uint8, device="cuda") for t in w.steps}
     efx = {t: cbs.calibatt_eps_fx(t, w.total_steps, w.eps_floor, w.eps_start, w.eps_rate)
            for t in w.steps}
-    t_energy = t_select = 0.0
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    grid = (w.grid.frames, w.grid.rows, w.grid.cols, 5)
+    prof = torch.empty(w.heads, w.grid.frames * w.grid.rows, R, dtype=torch.float32, device="cuda")
+    sim = torch.empty(w.heads, dtype=torch.float32, device="cuda")
+    sim_sum = torch.zeros(w.heads, dtype=torch.float64, device="cuda")
+    t_energy = t_select = t_sim = 0.0
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
     for p in range(draws):
         q, k = calib_draw(w, p, basis, "cuda")
         torch.cuda.synchronize()
         ev[0].record()
         cbs.calibatt_block_energy(q, k, energy, w.scale, ws)
         ev[1].record()
+        cbs.calibatt_spatial_similarity(ws, w.heads, w.n_tokens, grid, prof, sim)
+        ev[2].record()
         for t in w.steps:
             cbs.calibatt_build_mask(energy, efx[t], votes[t])
-        ev[2].record()
+        ev[3].record()
         torch.cuda.synchronize()
+        sim_sum += sim.double()
         t_energy += ev[0].elapsed_time(ev[1])
-        t_select += ev[1].elapsed_time(ev[2])
+        t_sim += ev[1].elapsed_time(ev[2])
+        t_select += ev[2].elapsed_time(ev[3])
+    s_mean = (sim_sum / draws).cpu().numpy()
     mask = torch.empty(w.heads, R, R, dtype=torch.uint8, device="cuda")
     off = torch.empty(w.heads * R + 1, dtype=torch.int32, device="cuda")
     idx = torch.empty(w.heads * R * R, dtype=torch.int32, device="cuda")
@@ -207,6 +216,10 @@ def calibration_case(cbs, draws: int):
         "energy_ms_per_draw": round(t_energy / draws, 3),
         "energy_tflops": round(flop_energy / (t_energy / draws * 1e-3) / 1e12, 1),
         "select_votes_ms_per_draw_3eps": round(t_select / draws, 3),
+        "similarity_ms_per_draw": round(t_sim / draws, 3),
+        "similarity_mean_min_max": [round(float(s_mean.mean()), 4), round(float(s_mean.min()), 4),
+                                    round(float(s_mean.max()), 4)],
+        "repeat_heads_at_gamma_0_87": int((s_mean > 0.87).sum()),
         "finalize_ms_3steps_incl_sync": round(t_fin, 3),
         "kept_fraction_by_step": {str(t): round(v, 4) for t, v in kept.items()},
     }

@@ -42,6 +42,8 @@ SIGNATURES = {
     "calibatt_block_energy_workspace": (_c.c_size_t, [_c.c_int32, _c.c_int32]),
     "calibatt_block_energy": (_c.c_int, [_p, _p, _p, _c.c_int32, _c.c_int32, _c.c_int32,
                                          _c.c_int64, _c.c_int64, _c.c_float, _p, _c.c_size_t, _p]),
+    "calibatt_spatial_similarity": (_c.c_int, [_p, _c.c_size_t, _c.c_int32, _c.c_int32, _p, _p,
+                                                _p, _p]),
     "calibatt_eps_fx": (_c.c_uint64, [_c.c_double] * 5),
     "calibatt_build_mask": (_c.c_int, [_p, _c.c_int32, _c.c_int32, _c.c_int32, _c.c_uint64, _p,
                                        _p, _p]),
@@ -248,6 +250,24 @@ def calibatt_block_energy(q, k, energy, scale: float, workspace=None, stream=Non
     _check("calibatt_block_energy", rc)
 
 
+def calibatt_spatial_similarity(energy_workspace, heads: int, n_tokens: int, grid, row_profiles,
+                                similarity, stream=None) -> None:
+    """row_profiles ([H][frames*rows][R] fp32 CUDA) and similarity ([H] fp32
+    CUDA) from the workspace of a preceding calibatt_block_energy call on the
+    same stream; grid = (frames, rows, cols, anchors)."""
+    for t in (row_profiles, similarity):
+        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("row_profiles and similarity must be contiguous float32 CUDA tensors")
+    R = n_blocks(n_tokens)
+    if row_profiles.numel() < heads * grid[0] * grid[1] * R or similarity.numel() < heads:
+        raise ValueError("row_profiles needs heads*frames*rows*R and similarity heads elements")
+    g = Grid(*[int(x) for x in grid])
+    rc = load_library().calibatt_spatial_similarity(
+        _ptr(energy_workspace), energy_workspace.numel() * energy_workspace.element_size(), heads,
+        n_tokens, ctypes.byref(g), _ptr(row_profiles), _ptr(similarity), _stream(stream))
+    _check("calibatt_spatial_similarity", rc)
+
+
 def calibatt_eps_fx(t: float, T: float, A: float, C: float, k: float) -> int:
     return int(load_library().calibatt_eps_fx(float(t), float(T), float(A), float(C), float(k)))
 
@@ -340,6 +360,20 @@ def sparse_attention(q, k, v, kv_offsets, kv_indices, scale: float, repeat_flags
     o = torch.empty_like(q)
     calibatt_sparse_attn_fwd(q, k, v, o, kv_offsets, kv_indices, scale, repeat_flags, grid, stream)
     return o
+
+
+def energy_and_similarity(q, k, scale: float, grid, stream=None):
+    """One Q K^T pass: (energy [H][R][R], similarity [H], row profiles
+    [H][frames*rows][R]) of q, k for grid (frames, rows, cols, anchors)."""
+    H, N, _ = q.shape
+    R = n_blocks(N)
+    e = torch.empty(H, R, R, dtype=torch.float32, device=q.device)
+    ws = torch.empty(max(calibatt_block_energy_workspace(H, N), 8), dtype=torch.uint8, device=q.device)
+    calibatt_block_energy(q, k, e, scale, ws, stream)
+    prof = torch.empty(H, grid[0] * grid[1], R, dtype=torch.float32, device=q.device)
+    sim = torch.empty(H, dtype=torch.float32, device=q.device)
+    calibatt_spatial_similarity(ws, H, N, grid, prof, sim, stream)
+    return e, sim, prof
 
 
 def block_energy(q, k, scale: float, stream=None) -> torch.Tensor:

@@ -67,7 +67,7 @@ extern "C" {
 
 const char* calibatt_last_error(void) { return calibatt::g_last_error.c_str(); }
 
-int32_t calibatt_abi_version(void) { return 5; }
+int32_t calibatt_abi_version(void) { return 6; }
 
 
 size_t calibatt_sparse_attn_fwd_workspace(int32_t heads, int32_t n_tokens) {
@@ -284,6 +284,54 @@ int calibatt_block_energy(const void* q, const void* k, float* energy, int32_t h
   a.n_blocks = (int32_t)R;
   a.heads = heads;
   hipError_t e = launch_block_energy(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return api_ok();
+}
+
+int calibatt_spatial_similarity(const void* energy_workspace, size_t workspace_bytes,
+                                int32_t heads, int32_t n_tokens, const calibatt_grid* grid,
+                                float* row_profiles, float* similarity, void* stream) {
+  const char* fn = "calibatt_spatial_similarity";
+  if (heads < 0 || n_tokens < 0)
+    return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: heads (%d) and n_tokens (%d) must be >= 0", fn,
+                    heads, n_tokens);
+  if (heads == 0 || n_tokens == 0) return api_ok();
+  if (!grid) return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: null grid", fn);
+  if (grid->frames <= 0 || grid->rows <= 0 || grid->cols <= 0 ||
+      (int64_t)grid->frames * grid->rows * grid->cols != n_tokens)
+    return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: grid %dx%dx%d does not cover N=%d", fn,
+                    grid->frames, grid->rows, grid->cols, n_tokens);
+  if (grid->anchors < 1 || grid->anchors > grid->rows)
+    return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: anchors %d not in [1, rows=%d]", fn,
+                    grid->anchors, grid->rows);
+  if (grid->cols > 8192)
+    return api_fail(CALIBATT_ERR_UNSUPPORTED, "%s: %d columns > 8192", fn, grid->cols);
+  const int64_t R = ceil_div(n_tokens, CALIBATT_BLOCK);
+  if (R > CALIBATT_MAX_BLOCKS)
+    return api_fail(CALIBATT_ERR_UNSUPPORTED, "%s: %lld blocks > %d", fn, (long long)R,
+                    CALIBATT_MAX_BLOCKS);
+  if ((int64_t)heads * grid->frames * grid->rows > 0x7fffffff)
+    return api_fail(CALIBATT_ERR_UNSUPPORTED, "%s: too many spatial rows", fn);
+  if (!row_profiles || !similarity)
+    return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: null row_profiles/similarity", fn);
+  const size_t need = calibatt_block_energy_workspace(heads, n_tokens);
+  if (!energy_workspace || workspace_bytes < need)
+    return api_fail(CALIBATT_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu", fn, workspace_bytes, need);
+  if (reinterpret_cast<uintptr_t>(energy_workspace) & 7u)
+    return api_fail(CALIBATT_ERR_WORKSPACE, "%s: workspace must be 8-byte aligned", fn);
+  SimArgs a;
+  a.partials = static_cast<const float*>(energy_workspace);
+  a.row_stats = a.partials + (size_t)2 * heads * R * R * CALIBATT_BLOCK;
+  a.profiles = row_profiles;
+  a.similarity = similarity;
+  a.heads = heads;
+  a.n_tokens = n_tokens;
+  a.n_blocks = (int32_t)R;
+  a.frames = grid->frames;
+  a.rows = grid->rows;
+  a.cols = grid->cols;
+  a.anchors = grid->anchors;
+  hipError_t e = launch_spatial_similarity(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, fn);
   return api_ok();
 }

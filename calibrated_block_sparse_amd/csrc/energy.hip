@@ -195,6 +195,110 @@ __global__ void __launch_bounds__(kThreads) energy_fixup_kernel(const EnergyArgs
   }
 }
 
+// ---------------------------------------------------------------------------
+// Spatial similarity of a head (zhichai.net article on CalibAtt, §二
+// observation 4 and §三: one score s per (t, l, h); the pages give no
+// formula). From the partials above: the profile of spatial row (f, y) is
+// rho[c] = (1/W) sum over its W query tokens i of P_i(block c), with
+// P_i(block c) = s_c(i) 2^(m_c(i) - m(i)) / l(i); s is the mean over frames
+// and non-anchor rows of cos(rho_{f,y}, rho_{f,a(y)}).
+
+// Butterfly sum over the 64 lanes (same order on every lane and call).
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+// One workgroup per (head, spatial row); wave w takes key blocks w, w+4, ...,
+// lane x the row's tokens x, x+64, ...
+__global__ void __launch_bounds__(kThreads) row_profile_kernel(const SimArgs a) {
+  extern __shared__ float s_row[];  // cols x (m, 1/l)
+  const int R = a.n_blocks, W = a.cols, FR = a.frames * a.rows;
+  const int head = blockIdx.x / FR, fy = blockIdx.x - head * FR;
+  const int64_t np = (int64_t)R * kBlock;
+  const int64_t i0 = (int64_t)fy * W;
+  const float2* __restrict__ st = reinterpret_cast<const float2*>(a.row_stats) + (int64_t)head * np + i0;
+  for (int x = threadIdx.x; x < W; x += kThreads) {
+    const float2 v = st[x];
+    s_row[2 * x] = v.x;
+    s_row[2 * x + 1] = 1.f / v.y;
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const float2* __restrict__ part = reinterpret_cast<const float2*>(a.partials) + (int64_t)head * R * np + i0;
+  float* out = a.profiles + ((int64_t)head * FR + fy) * R;
+  const float inv_w = 1.f / (float)W;
+  for (int c = wave; c < R; c += kThreads / 64) {
+    const float2* p = part + (int64_t)c * np;
+    float acc = 0.f;
+    for (int x = lane; x < W; x += 64) {
+      const float2 v = p[x];
+      acc = __builtin_fmaf(v.x, __builtin_ldexpf(s_row[2 * x + 1], (int)(v.y - s_row[2 * x])), acc);
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) out[c] = acc * inv_w;
+  }
+}
+
+// One workgroup per head; wave w takes the spatial rows w, w+4, ... of all
+// frames (in order), lanes the key blocks; per-wave sums are combined in
+// wave order.
+__global__ void __launch_bounds__(kThreads) similarity_kernel(const SimArgs a) {
+  __shared__ float s_sum[kThreads / 64];
+  __shared__ int s_cnt[kThreads / 64];
+  const int R = a.n_blocks, FR = a.frames * a.rows;
+  const int head = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const float* prof = a.profiles + (int64_t)head * FR * R;
+  float total = 0.f;
+  int count = 0;
+  for (int fy = wave; fy < FR; fy += kThreads / 64) {
+    const int f = fy / a.rows, y = fy - f * a.rows;
+    const int m = y * a.anchors / a.rows;
+    const int ay = (2 * m + 1) * a.rows / (2 * a.anchors);  // anchor row of y's segment
+    if (ay == y) continue;
+    const float* u = prof + (int64_t)fy * R;
+    const float* w = prof + (int64_t)(f * a.rows + ay) * R;
+    float dot = 0.f, uu = 0.f, ww = 0.f;
+    for (int c = lane; c < R; c += 64) {
+      dot = __builtin_fmaf(u[c], w[c], dot);
+      uu = __builtin_fmaf(u[c], u[c], uu);
+      ww = __builtin_fmaf(w[c], w[c], ww);
+    }
+    dot = wave_sum(dot);
+    uu = wave_sum(uu);
+    ww = wave_sum(ww);
+    total += dot / __builtin_sqrtf(uu * ww);
+    ++count;
+  }
+  if (lane == 0) {
+    s_sum[wave] = total;
+    s_cnt[wave] = count;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float t = 0.f;
+    int n = 0;
+    for (int w = 0; w < kThreads / 64; ++w) {
+      t += s_sum[w];
+      n += s_cnt[w];
+    }
+    a.similarity[head] = n == 0 ? 1.f : t / (float)n;
+  }
+}
+
+hipError_t launch_spatial_similarity(const SimArgs& a, hipStream_t stream) {
+  const int64_t items = (int64_t)a.heads * a.frames * a.rows;
+  if (items <= 0) return hipSuccess;
+  hipLaunchKernelGGL(row_profile_kernel, dim3((unsigned)items), dim3(kThreads),
+                     (size_t)a.cols * 2 * sizeof(float), stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(similarity_kernel, dim3(a.heads), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_block_energy(const EnergyArgs& a, hipStream_t stream) {
   const int items = a.heads * a.n_blocks;
   if (items <= 0) return hipSuccess;

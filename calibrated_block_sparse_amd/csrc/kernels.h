@@ -56,6 +56,15 @@ struct EnergyArgs {
   int32_t heads;
 };
 
+struct SimArgs {
+  const float* partials;     // energy workspace: float2 [heads][R][R*128]
+  const float* row_stats;    // energy workspace: float2 [heads][R*128]
+  float* profiles;           // [heads][frames*rows][R]
+  float* similarity;         // [heads]
+  int32_t heads, n_tokens, n_blocks;
+  int32_t frames, rows, cols, anchors;
+};
+
 // Error reporting of the C ABI (thread-local message, returned status).
 int api_fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 int api_ok();
@@ -63,6 +72,7 @@ int api_ok();
 hipError_t launch_v_transpose(const VtArgs& a, hipStream_t stream);
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_block_energy(const EnergyArgs& a, hipStream_t stream);
+hipError_t launch_spatial_similarity(const SimArgs& a, hipStream_t stream);
 hipError_t launch_mfma_probe(float* sink, int64_t iters, int32_t workgroups, hipStream_t stream);
 
 hipError_t launch_select_votes(const float* energy, int32_t n_draws, int32_t heads,

@@ -69,7 +69,8 @@ const char* calibatt_last_error(void);
  * added the workspace of calibatt_sparse_attn_fwd, version 3 its two halves
  * calibatt_prepare_vt and calibatt_sparse_attn_fwd_vt, version 4 the
  * single-pass energy workspace and calibatt_mfma_rate_probe, version 5 the
- * mask bank (calibatt_bank_*) and CALIBATT_ERR_IO. */
+ * mask bank (calibatt_bank_*) and CALIBATT_ERR_IO, version 6
+ * calibatt_spatial_similarity. */
 int32_t calibatt_abi_version(void);
 
 /*
@@ -173,6 +174,32 @@ int calibatt_block_energy(const void* q, const void* k, float* energy,
                           int32_t heads, int32_t n_tokens, int32_t head_dim,
                           int64_t stride_head, int64_t stride_token, float scale,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Spatial similarity score of each head ([CalibAtt blog] §二 observation 4:
+ * the spatial rows of a frame attend alike; §三: a score s per (t, l, h), a
+ * head above gamma = 0.87 computes only k anchor rows per frame). The pages
+ * give no formula; the reading implemented:
+ *   profile of spatial row (f, y): rho[c] = (1/cols) * sum over the row's
+ *     cols query tokens i of sum_{j in J_c} P_ij  (P as for the energy);
+ *   s[h] = mean over frames f and non-anchor rows y of the cosine of
+ *     rho_{f,y} and rho_{f,a(y)}, anchors A(m) = floor((2m+1) rows / (2k)),
+ *     a(y) = A(floor(y k / rows)) (as for repeat heads); 1 when every row is
+ *     an anchor.
+ * It reads the partial sums calibatt_block_energy leaves in its workspace:
+ * call it after calibatt_block_energy for the same q, k, heads and N on the
+ * same stream, with that workspace, before the workspace is reused (one
+ * Q K^T pass serves both). Averaging over prompts and the comparison with
+ * gamma are the caller's.
+ *
+ *   energy_workspace  device, as filled by calibatt_block_energy
+ *   grid              frames*rows*cols == N, 1 <= anchors <= rows, cols <= 8192
+ *   row_profiles      device fp32 [heads][frames*rows][R], output
+ *   similarity        device fp32 [heads], output
+ */
+int calibatt_spatial_similarity(const void* energy_workspace, size_t workspace_bytes,
+                                int32_t heads, int32_t n_tokens, const calibatt_grid* grid,
+                                float* row_profiles, float* similarity, void* stream);
 
 /*
  * Threshold eps(t) = A + (C - A) * exp(-k * t / T) ([CalibAtt blog] §三)

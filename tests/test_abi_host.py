@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version(lib):
-    assert cbs.calibatt_abi_version() == 5
+    assert cbs.calibatt_abi_version() == 6
 
 
 def fake(n=16):
@@ -115,6 +115,22 @@ def test_mask_argument_errors(lib):
                                                        fake(), None, None)
     assert fin(0, 1, 2) == -1 and fin(256, 1, 2) == -1 and fin(64, 3, 2) == -1 and fin(64, 1, 0) == -1
     assert lib.calibatt_compile_skiplist(fake(), 40, 8000, fake(), fake(), None, None) == -2
+
+
+def test_similarity_argument_errors(lib):
+    H, N = 2, 1000
+    ws = cbs.calibatt_block_energy_workspace(H, N)
+    good = cbs.Grid(2, 20, 25, 5)
+    f = lambda **kw: lib.calibatt_spatial_similarity(kw.get("ws", fake()), kw.get("wsb", ws), H,
+                                                     kw.get("n", N), kw.get("g", ctypes.byref(good)),
+                                                     kw.get("prof", fake()), fake(), None)
+    assert f(g=None) == -1
+    assert f(g=ctypes.byref(cbs.Grid(2, 20, 24, 5))) == -1          # does not cover N
+    assert f(g=ctypes.byref(cbs.Grid(2, 20, 25, 21))) == -1         # anchors > rows
+    assert f(prof=None) == -1
+    assert f(wsb=ws - 1) == -4
+    assert f(ws=None) == -4
+    assert lib.calibatt_spatial_similarity(None, 0, 0, N, None, None, None, None) == 0
 
 
 def test_mfma_probe_argument_errors(lib):

@@ -189,3 +189,81 @@ def test_calibration_end_to_end_small(gpu):
         same_rows = (vg == votes_o[t]).all(axis=-1)
         assert np.array_equal(mask.cpu().numpy()[same_rows], want[same_rows])
         say(f"  t={t}: kept fraction {nnz / (w.heads * R * R):.3f}")
+
+
+# ----------------------------------------------------------------------------
+# Spatial similarity (calibatt_spatial_similarity after calibatt_block_energy).
+# Bars: row profiles per element within 1e-4 relative + 1e-7 absolute (the
+# energy bar), s within 1e-5 absolute.
+
+
+def gpu_similarity(cbs, q, k, scale, grid):
+    e, s, prof = cbs.energy_and_similarity(q, k, scale, grid)
+    torch.cuda.synchronize()
+    return f64(s), f64(prof)
+
+
+@pytest.mark.parametrize("F,Hs,W,kk,H,std", [(2, 20, 25, 5, 2, 1.5), (1, 8, 32, 2, 1, 1.0),
+                                             (3, 10, 13, 3, 2, 2.5), (2, 30, 7, 5, 1, 4.0)])
+def test_similarity_matches_oracle(gpu, F, Hs, W, kk, H, std):
+    N = F * Hs * W
+    say(f"case similarity F={F} rows={Hs} cols={W} anchors={kk} H={H} std={std}")
+    q = gaussian_bf16(300 + N, (H, N, 128), std=std).to(DEV)
+    k = gaussian_bf16(301 + N, (H, N, 128)).to(DEV)
+    scale = 1 / np.sqrt(128)
+    s, prof = gpu_similarity(gpu, q, k, scale, (F, Hs, W, kk))
+    for h in range(H):
+        qb, kb = bf16_bits(q[h]), bf16_bits(k[h])
+        want_p = oracle.row_profiles(qb, kb, scale, F, Hs, W)
+        err = np.abs(prof[h] - want_p)
+        assert (err <= 1e-4 * np.abs(want_p) + 1e-7).all(), f"head {h}: profile max err {err.max():.2e}"
+        want_s = oracle.spatial_similarity(qb, kb, scale, F, Hs, W, kk)
+        assert abs(s[h] - want_s) < 1e-5, (h, s[h], want_s)
+        say(f"  head {h}: s {s[h]:.6f} (oracle {want_s:.6f})")
+
+
+def test_similarity_closed_forms(gpu):
+    say("case similarity closed forms")
+    # one-hot attention (see the oracle pin): s = 4/6
+    F, Hs, W = 1, 8, 32
+    N = F * Hs * W
+    pattern = [0, 0, 0, 1, 1, 0, 1, 1]
+    k = torch.zeros(1, N, 128)
+    k[0, :128, 0] = 1.0
+    k[0, 128:, 1] = 1.0
+    q = torch.zeros(1, N, 128)
+    for y in range(Hs):
+        q[0, y * W:(y + 1) * W, pattern[y]] = 64.0
+    s, prof = gpu_similarity(gpu, q.to(torch.bfloat16).to(DEV), k.to(torch.bfloat16).to(DEV), 1.0,
+                             (F, Hs, W, 2))
+    np.testing.assert_allclose(prof[0], np.eye(2)[pattern], atol=1e-6)
+    assert abs(s[0] - 4 / 6) < 1e-6
+    # Q = 0: all profiles |J_c| / N, s = 1
+    F, Hs, W = 2, 5, 40
+    k = gaussian_bf16(320, (2, F * Hs * W, 128)).to(DEV)
+    s, prof = gpu_similarity(gpu, torch.zeros_like(k), k, 0.1, (F, Hs, W, 2))
+    np.testing.assert_allclose(prof, np.broadcast_to(np.array([128, 128, 128, 16]) / 400, prof.shape),
+                               rtol=1e-6)
+    np.testing.assert_allclose(s, 1.0, atol=1e-6)
+    # every row an anchor: s = 1 exactly
+    s, _ = gpu_similarity(gpu, gaussian_bf16(321, (1, 128, 128)).to(DEV),
+                          gaussian_bf16(322, (1, 128, 128)).to(DEV), 0.1, (1, 4, 32, 4))
+    assert s[0] == 1.0
+
+
+def test_similarity_calibration_shape_small(gpu):
+    """The small calibration recipe (low-rank positional code): one draw,
+    every head against the oracle, then the classification at gamma."""
+    w = CALIB_WORKLOADS["calibration_small"]
+    g = w.grid
+    grid = (g.frames, g.rows, g.cols, 5)
+    say(f"case similarity calibration_small H={w.heads} N={w.n_tokens}")
+    basis = calib_basis(w, "cpu")
+    q, k = calib_draw(w, 0, basis, "cpu")
+    s, _ = gpu_similarity(gpu, q.to(DEV), k.to(DEV), w.scale, grid)
+    want = np.array([oracle.spatial_similarity(bf16_bits(q[h]), bf16_bits(k[h]), w.scale, *grid)
+                     for h in range(w.heads)])
+    np.testing.assert_allclose(s, want, atol=1e-5)
+    assert np.array_equal(oracle.classify_repeat(s), oracle.classify_repeat(want)) or \
+        np.min(np.abs(want - oracle.GAMMA)) < 1e-5
+    say(f"  s = {np.round(s, 4).tolist()}")
