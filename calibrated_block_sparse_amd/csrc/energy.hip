@@ -241,19 +241,21 @@ __global__ void __launch_bounds__(kThreads) row_profile_kernel(const SimArgs a) 
   }
 }
 
-// One workgroup per head; wave w takes the spatial rows w, w+4, ... of all
-// frames (in order), lanes the key blocks; per-wave sums are combined in
-// wave order.
-__global__ void __launch_bounds__(kThreads) similarity_kernel(const SimArgs a) {
-  __shared__ float s_sum[kThreads / 64];
-  __shared__ int s_cnt[kThreads / 64];
+// One workgroup of 16 waves per head; wave w takes the spatial rows w,
+// w+16, ... of all frames (in order), lanes the key blocks; per-wave sums
+// are combined in wave order.
+constexpr int kSimThreads = 1024;
+
+__global__ void __launch_bounds__(kSimThreads) similarity_kernel(const SimArgs a) {
+  __shared__ float s_sum[kSimThreads / 64];
+  __shared__ int s_cnt[kSimThreads / 64];
   const int R = a.n_blocks, FR = a.frames * a.rows;
   const int head = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const float* prof = a.profiles + (int64_t)head * FR * R;
   float total = 0.f;
   int count = 0;
-  for (int fy = wave; fy < FR; fy += kThreads / 64) {
+  for (int fy = wave; fy < FR; fy += kSimThreads / 64) {
     const int f = fy / a.rows, y = fy - f * a.rows;
     const int m = y * a.anchors / a.rows;
     const int ay = (2 * m + 1) * a.rows / (2 * a.anchors);  // anchor row of y's segment
@@ -280,7 +282,7 @@ __global__ void __launch_bounds__(kThreads) similarity_kernel(const SimArgs a) {
   if (threadIdx.x == 0) {
     float t = 0.f;
     int n = 0;
-    for (int w = 0; w < kThreads / 64; ++w) {
+    for (int w = 0; w < kSimThreads / 64; ++w) {
       t += s_sum[w];
       n += s_cnt[w];
     }
@@ -295,7 +297,7 @@ hipError_t launch_spatial_similarity(const SimArgs& a, hipStream_t stream) {
                      (size_t)a.cols * 2 * sizeof(float), stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(similarity_kernel, dim3(a.heads), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL(similarity_kernel, dim3(a.heads), dim3(kSimThreads), 0, stream, a);
   return hipGetLastError();
 }
 
