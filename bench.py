@@ -346,6 +346,15 @@ def main():
                      "kernel_ms_mean": round(per_launch_ms, 4), "kernel_hash": kernel_hash()},
         "v_transpose_ms_mean": round(float(np.mean(sp["prep_ms"])), 4),
     }
+    if out["roofline"]["traffic"]:
+        out["roofline"]["achieved_hbm_gbs"] = round(out["roofline"]["traffic"] / (per_launch_ms * 1e-3) / 1e9, 1)
+    # the pages' own end-to-end numbers (video generation, hardware and precision
+    # not stated): context only, not comparable with a kernel rate
+    out["pages_context_end_to_end"] = {
+        "wan21_14b_720p": {"dense_s": 1244, "calibatt_s": 785, "speedup": 1.58, "block_sparsity": 0.625},
+        "wan21_14b_480p": {"dense_s": 363, "calibatt_s": 250, "speedup": 1.45, "block_sparsity": 0.681},
+        "mochi1_480p": {"dense_s": 188, "calibatt_s": 161, "speedup": 1.16, "block_sparsity": 0.691},
+    }
     log("[bench] matrix-core rate probe")
     onbox, probe_ms = mfma_probe_case(cbs)
     out["roofline"]["onbox_mfma_loop_tflops"] = round(onbox, 1)
