@@ -239,3 +239,56 @@ def test_mfma_rate_probe(gpu):
     say(f"  mfma probe: {tflops:.0f} TFLOP/s")
     assert 251.7 < tflops < 2516.6 * 1.02
     assert float(sink[0]) == 0.0
+
+
+def test_more_heads_than_one_launch(gpu):
+    """300 heads (launches hold at most 256), every seventh a repeat head:
+    each head against the oracle."""
+    F, Hs, W, kk = 2, 4, 32, 2
+    N, H = F * Hs * W, 300
+    say(f"case {H} heads N={N}")
+    q, k, v = (gaussian_bf16(400 + i, (H, N, 128)).to(DEV) for i in range(3))
+    R = n_blocks(N)
+    mask = bernoulli_mask(404, H, R, 0.5, diagonal=True)
+    flags = (np.arange(H) % 7 == 6).astype(np.uint8)
+    o, _, _ = run(gpu, q, k, v, mask, 0.1, flags, (F, Hs, W, kk))
+    for h in range(H):
+        qb, kb, vb = (bf16_bits(t[h]) for t in (q, k, v))
+        if flags[h]:
+            want = oracle.repeat_head_attention(qb, kb, vb, 0.1, F, Hs, W, kk)
+        else:
+            want = oracle.block_sparse_attention(qb, kb, vb, 0.1, mask[h])
+        assert_attn_close(f64(o[h]), want, f"head {h}")
+
+
+def test_out_of_range_entries_are_skipped(gpu):
+    """Indices outside [0, R) are skipped and offsets are clamped to
+    [0, nnz): the output equals the oracle over the in-range entries."""
+    N, H = 700, 2
+    R = n_blocks(N)
+    say(f"case out-of-range list entries N={N}")
+    q, k, v = (gaussian_bf16(410 + i, (H, N, 128)).to(DEV) for i in range(3))
+    mask = bernoulli_mask(414, H, R, 0.5, diagonal=True)
+    off, idx = oracle.compile_skiplist(mask)
+    # insert -1, R and R+7 after the first entry of every row (still "ascending" order is not needed)
+    new_idx, new_off = [], [0]
+    for row in range(H * R):
+        ent = idx[off[row]:off[row + 1]].tolist()
+        ent = ent[:1] + [-1, R, R + 7] + ent[1:]
+        new_idx += ent
+        new_off.append(len(new_idx))
+    nnz = len(new_idx)
+    off_t = torch.tensor(new_off, dtype=torch.int32, device=DEV)
+    idx_t = torch.tensor(new_idx, dtype=torch.int32, device=DEV)
+    o = torch.empty_like(q)
+    gpu.calibatt_sparse_attn_fwd(q, k, v, o, off_t, idx_t, 0.1)
+    # offsets past nnz: the last row's range is clamped to [.., nnz)
+    off_big = off_t.clone()
+    off_big[-1] = nnz + 1000
+    o2 = torch.empty_like(q)
+    gpu.calibatt_sparse_attn_fwd(q, k, v, o2, off_big, idx_t, 0.1)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2)
+    for h in range(H):
+        want = oracle.block_sparse_attention(*(bf16_bits(t[h]) for t in (q, k, v)), 0.1, mask[h])
+        assert_attn_close(f64(o[h]), want, f"head {h}")
