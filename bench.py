@@ -113,6 +113,69 @@ def attn_case(cbs, name: str, steps: int, warmup: int, dense: bool = False, mask
                 prep_ms=per[:, 0], total_ms=total, mask=mask, tensors=(q, k, v))
 
 
+def bank_case(cbs, case, steps: int = 50, layers: int = 40, reps: int = 20):
+    """Mask bank at the layer's shape: a steps x layers bank whose (t, l)
+    share three entries (the layer's mask and two reshuffles of its heads),
+    written, opened and uploaded; then the host cost of a lookup and of a
+    CalibAttention call against the direct call with the same lists."""
+    import tempfile
+    from calibrated_block_sparse_amd.bank import CalibAttention, MaskBank, write_bank
+    w = case["workload"]
+    mask = case["mask"]
+    q, k, v = case["tensors"]
+    entries = []
+    for e in range(3):
+        m = mask if e == 0 else mask[np.random.default_rng(e).permutation(w.heads)]
+        off, idx = cbs.compile_skiplist(torch.from_numpy(np.ascontiguousarray(m)).cuda())
+        entries.append((off.cpu().numpy(), idx.cpu().numpy(), None))
+    entry_of = [[(t * layers + l) % 3 for l in range(layers)] for t in range(steps)]
+    with tempfile.TemporaryDirectory() as d:
+        path = os.path.join(d, "bank.cbsm")
+        t0 = time.perf_counter()
+        write_bank(path, steps, layers, w.heads, w.n_tokens, entry_of, entries)
+        t_write = time.perf_counter() - t0
+        size = os.path.getsize(path)
+        t0 = time.perf_counter()
+        bank = MaskBank(path, device="cuda")
+        torch.cuda.synchronize()
+        t_open = time.perf_counter() - t0
+    n = 20000
+    t0 = time.perf_counter()
+    for i in range(n):
+        bank.lookup(i % steps, (i // steps) % layers)
+    t_lookup = (time.perf_counter() - t0) / n
+    attn = CalibAttention(bank, w.scale)
+    lk = bank.lookup(0, 0)
+    o = torch.empty_like(q)
+    ws = torch.empty(cbs.calibatt_sparse_attn_fwd_workspace(w.heads, w.n_tokens), dtype=torch.uint8,
+                     device="cuda")
+
+    def via_bank():
+        return attn(q, k, v, 0, 0)
+
+    def direct():
+        cbs.calibatt_sparse_attn_fwd(q, k, v, o, lk.kv_offsets, lk.kv_indices, w.scale, workspace=ws)
+
+    ms = {}
+    for name, fn in (("bank", via_bank), ("direct", direct)):
+        fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        ms[name] = (time.perf_counter() - t0) * 1e3 / reps
+    out_bank = via_bank()
+    direct()
+    torch.cuda.synchronize()
+    bank.close()
+    return {"steps_x_layers": [steps, layers], "entries": 3, "file_mb": round(size / 2 ** 20, 2),
+            "write_s": round(t_write, 3), "open_upload_s": round(t_open, 3),
+            "lookup_us": round(t_lookup * 1e6, 2),
+            "attention_ms_via_bank": round(ms["bank"], 3), "attention_ms_direct": round(ms["direct"], 3),
+            "bitwise_equal": bool(torch.equal(out_bank, o))}
+
+
 SWEEP_FRACTIONS = (1.0, 0.75, 0.5, 0.375, 0.25, 0.125)
 
 
@@ -373,6 +436,8 @@ def main():
             extras[name] = {"ms": round(m, 3), "pairs": c["pairs"],
                             "effective_tflops": round(c["pairs"] * PAIR_FLOP / (m * 1e-3) / 1e12, 1)}
             del c
+        log("[bench] extra: mask bank")
+        extras["mask_bank"] = bank_case(cbs, sp)
         log(f"[bench] extra: calibration, {args.calib_draws} draws")
         extras["calibration"] = calibration_case(cbs, args.calib_draws)
         out["extras"] = extras
