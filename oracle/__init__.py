@@ -26,7 +26,7 @@ reading by closed forms.
 from .attention import (  # noqa: F401
     BLOCK, as_f64, dense_attention, kept_keys, block_sparse_attention_block,
     block_sparse_attention, anchor_rows, anchor_of_row, repeat_source_token,
-    repeat_head_attention,
+    repeat_head_attention, repeat_head_attention_masked,
 )
 from .calibration import (  # noqa: F401
     FX_BITS, block_energy_row, block_energy, quantize_energy, eps_schedule,

@@ -131,3 +131,27 @@ def repeat_head_attention(q, k, v, scale: float, frames: int, rows: int,
     uniq, inv = np.unique(src, return_inverse=True)
     o = _attend(q[uniq], k, v, scale)
     return o[inv]
+
+
+def repeat_head_attention_masked(q, k, v, scale: float, frames: int, rows: int, cols: int,
+                                 anchors: int, mask, tokens=None) -> np.ndarray:
+    """Repeat head that also keeps its block mask (a variant the pages leave
+    open: [CalibAtt blog] §三 names no mask for repeat heads). Every token
+    takes the output of its frame's anchor-row query at the same column, as
+    in repeat_head_attention, but that anchor query n attends only to the keys
+    of the blocks its own block-row floor(n / 128) keeps (mask [R][R]); an
+    anchor query whose row keeps nothing yields zeros."""
+    q, k, v = as_f64(q), as_f64(k), as_f64(v)
+    N = q.shape[0]
+    assert frames * rows * cols == N
+    mask = np.asarray(mask)
+    toks = np.arange(N) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    src = repeat_source_token(toks, frames, rows, cols, anchors)
+    uniq, inv = np.unique(src, return_inverse=True)
+    out = np.zeros((uniq.size, q.shape[1]))
+    for r in np.unique(uniq // BLOCK):
+        sel = np.flatnonzero(uniq // BLOCK == r)
+        keys = kept_keys(np.flatnonzero(mask[r]), N)
+        if keys.size:
+            out[sel] = _attend(q[uniq[sel]], k[keys], v[keys], scale)
+    return out[inv]

@@ -164,3 +164,47 @@ def test_repeat_head_anchor_rows_are_dense_and_copies_exact():
         np.testing.assert_allclose(o[:, y], d[:, y], rtol=1e-12, atol=1e-12)
     for y in range(Hs):
         assert np.array_equal(o[:, y], o[:, 3 + 6 * (y // 6)])
+
+
+# Repeat head that also keeps its block mask (a variant; the pages name no
+# mask for repeat heads): pinned to torch's fp64 SDPA with the token mask the
+# block mask implies.
+
+
+def token_mask(mask, N):
+    b = np.arange(N) // oracle.BLOCK
+    return mask[b][:, b].astype(bool)
+
+
+def test_masked_repeat_anchor_rows_equal_masked_sdpa():
+    F, Hs, W = 2, 12, 20                       # N = 480, R = 4 (last block 96 keys)
+    N = F * Hs * W
+    R = -(-N // 128)
+    q, k, v = rnd(41, N, 128), rnd(42, N, 128), rnd(43, N, 128)
+    mask = (np.random.default_rng(44).random((R, R)) < 0.5).astype(np.uint8)
+    np.fill_diagonal(mask, 1)
+    o = oracle.repeat_head_attention_masked(q, k, v, 0.1, F, Hs, W, 3, mask).reshape(F, Hs, W, 128)
+    d = sdpa(q, k, v, 0.1, token_mask(mask, N)).reshape(F, Hs, W, 128)
+    anchors = oracle.anchor_rows(Hs, 3)
+    for y in anchors:
+        np.testing.assert_allclose(o[:, y], d[:, y], rtol=1e-12, atol=1e-12)
+    a = oracle.anchor_of_row(Hs, 3)
+    for y in range(Hs):
+        assert np.array_equal(o[:, y], o[:, a[y]])
+
+
+def test_masked_repeat_full_mask_is_plain_repeat_and_empty_row_is_zero():
+    F, Hs, W = 1, 8, 40                        # N = 320, R = 3
+    N = F * Hs * W
+    q, k, v = rnd(45, N, 128), rnd(46, N, 128), rnd(47, N, 128)
+    full = np.ones((3, 3), np.uint8)
+    np.testing.assert_allclose(oracle.repeat_head_attention_masked(q, k, v, 0.1, F, Hs, W, 2, full),
+                               oracle.repeat_head_attention(q, k, v, 0.1, F, Hs, W, 2),
+                               rtol=1e-12, atol=1e-12)
+    m = full.copy()
+    m[1] = 0                                   # block-row 1 keeps nothing
+    o = oracle.repeat_head_attention_masked(q, k, v, 0.1, F, Hs, W, 2, m)
+    src = oracle.repeat_source_token(np.arange(N), F, Hs, W, 2)
+    zero = src // 128 == 1
+    assert zero.any() and not o[zero].any()
+    assert np.abs(o[~zero]).sum() > 0
