@@ -79,7 +79,7 @@ def time_launches(fns, steps: int, warmup: int):
 
 
 def attn_case(cbs, name: str, steps: int, warmup: int, dense: bool = False, mask=None,
-              tensors=None):
+              tensors=None, repeat_value: int = 1):
     from synth import ATTN_WORKLOADS, block_mask, qkv, repeat_flags
     w = ATTN_WORKLOADS[name]
     q, k, v = tensors if tensors is not None else qkv(w, device="cuda")
@@ -87,14 +87,14 @@ def attn_case(cbs, name: str, steps: int, warmup: int, dense: bool = False, mask
     if mask is None:
         mask = np.ones((w.heads, w.n_blocks, w.n_blocks), np.uint8) if dense else block_mask(w)
     off, idx = cbs.compile_skiplist(torch.from_numpy(mask).cuda())
-    flags = repeat_flags(w)
+    flags = repeat_flags(w) * repeat_value
     grid = None
     if flags.any():
         grid = (w.grid.frames, w.grid.rows, w.grid.cols, w.anchors)
     else:
         flags = None
     pairs = int(idx.numel()) if flags is None else int(
-        mask[flags == 0].sum() + int(flags.sum()) * -(-(w.grid.frames * w.anchors * w.grid.cols) // 128) * w.n_blocks)
+        mask[flags == 0].sum() + int((flags != 0).sum()) * -(-(w.grid.frames * w.anchors * w.grid.cols) // 128) * w.n_blocks)
 
     ws = torch.empty(cbs.calibatt_sparse_attn_fwd_workspace(w.heads, w.n_tokens), dtype=torch.uint8,
                      device="cuda")
@@ -436,6 +436,12 @@ def main():
             extras[name] = {"ms": round(m, 3), "pairs": c["pairs"],
                             "effective_tflops": round(c["pairs"] * PAIR_FLOP / (m * 1e-3) / 1e12, 1)}
             del c
+        log("[bench] extra: masked repeat heads (Mochi 480p)")
+        c = attn_case(cbs, "mochi1_480p_layer", 10, 3, repeat_value=2)
+        extras["mochi1_480p_layer_masked_repeat"] = {
+            "ms": round(float(np.median(c["per_ms"])), 3),
+            "plain_repeat_ms": extras.get("mochi1_480p_layer", {}).get("ms")}
+        del c
         log("[bench] extra: mask bank")
         extras["mask_bank"] = bank_case(cbs, sp)
         log(f"[bench] extra: calibration, {args.calib_draws} draws")

@@ -77,6 +77,17 @@ __device__ __forceinline__ void pipeline_reads() {
   }
 }
 
+// Items, in launch order: tiles of masked repeat heads (repeat heads that
+// also keep their block mask, a variant the pages leave open: anchor query
+// n attends only to the blocks its own block-row floor(n / 128) keeps), of
+// plain repeat heads, then query blocks of block-sparse heads. A masked tile
+// builds, in LDS behind the two tiles, a bitmap of kept blocks per query and
+// the ascending union of its queries' lists, walks the union, and drops a
+// block for a query outside its row by moving that query's reference to
+// +inf for the block (its exponentials are exactly 0). kAnyMasked is false
+// for launches without masked repeat heads, which then compile to the
+// plain loop.
+template <bool kAnyMasked>
 __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const AttnArgs a) {
   // Dynamic LDS (2 tiles): its contents are written by the copy engine
   // behind the compiler's back, so it must not be a static object the
@@ -94,6 +105,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const AttnArgs a)
   const int item = xcd_remap(blockIdx.x, a.n_items);
   const int rep_items = a.n_rep * a.rep_tiles;
   const bool rep = item < rep_items;
+  const bool masked = kAnyMasked && item < a.n_mrep * a.rep_tiles;   // heads[0 .. n_mrep) are masked
   int head, tile;
   if (rep) {
     head = a.heads[item / a.rep_tiles];
@@ -141,7 +153,51 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const AttnArgs a)
 
   // ---- kept-block range [beg, end): list positions (sparse) or blocks (repeat)
   int beg = 0, end = R;
-  if (!rep) {
+  // masked repeat tiles: per-query bitmaps [128][W] words, their union [W],
+  // the union as an ascending list [R] and its length
+  const int W = a.mask_words;
+  uint32_t* const bm = reinterpret_cast<uint32_t*>(smem + 2 * kTileBytes);
+  uint16_t* const ul = reinterpret_cast<uint16_t*>(bm + 129 * W);
+  const int qidx = wave * 32 + l32;
+  if (masked) {
+    uint32_t* const ub = bm + 128 * W;
+    uint32_t* const cnt = reinterpret_cast<uint32_t*>(ul) + (R + 1) / 2;
+    for (int i = tid; i < 129 * W; i += kThreads) bm[i] = 0u;
+    __syncthreads();
+    if (g == 0 && qvalid) {
+      const int64_t row = (int64_t)head * R + qtok / kBlock;
+      int64_t b = a.offsets[row], e = a.offsets[row + 1];
+      b = b < 0 ? 0 : (b > a.nnz ? a.nnz : b);
+      e = e < b ? b : (e > a.nnz ? a.nnz : e);
+      for (int64_t i = b; i < e; ++i) {
+        const int cc = a.indices[i];
+        if ((unsigned)cc >= (unsigned)R) continue;
+        const uint32_t bit = 1u << (cc & 31);
+        bm[qidx * W + (cc >> 5)] |= bit;
+        atomicOr(&ub[cc >> 5], bit);
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {  // compaction of the union (W <= 64 words)
+      uint32_t wv = lane < W ? ub[lane] : 0u;
+      const int n = __builtin_popcount(wv);
+      int incl = n;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += t;
+      }
+      int pos = incl - n;
+      while (wv) {
+        const int bit = __builtin_ctz(wv);
+        ul[pos++] = (uint16_t)(lane * 32 + bit);
+        wv &= wv - 1u;
+      }
+      if (lane == 63) *cnt = (uint32_t)incl;
+    }
+    __syncthreads();
+    end = (int)__builtin_amdgcn_readfirstlane(*cnt);
+  } else if (!rep) {
     const int64_t row = (int64_t)head * R + tile;
     int64_t b = a.offsets[row], e = a.offsets[row + 1];
     b = b < 0 ? 0 : (b > a.nnz ? a.nnz : b);
@@ -155,7 +211,12 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const AttnArgs a)
   // (constant address space), which the tile copies do not wait behind.
   const __attribute__((address_space(4))) int32_t* idx4 =
       (const __attribute__((address_space(4))) int32_t*)a.indices;
-  auto block_at = [&](int it) -> int { return rep ? it : idx4[it]; };
+  auto block_at = [&](int it) -> int {
+    if (masked) return (int)__builtin_amdgcn_readfirstlane(ul[it]);
+    return rep ? it : idx4[it];
+  };
+  // whether this lane's query keeps the current block (masked repeat tiles)
+  bool member = true;
 
   const CopyPlan cp = make_copy_plan(st, lane);
   const CopyPlan cpt = make_copy_plan(kBlock, lane);   // V^T tiles: 256-byte rows
@@ -279,7 +340,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const AttnArgs a)
   // first block; then the block max is found, the output rescaled and the
   // block recomputed from the K tile still in LDS.
   auto scores_probs = [&](bf16x8 (&pf)[8]) -> float {
-    const float mref = m_run == -__builtin_inff() ? 0.f : m_run;
+    const float mref = !member ? __builtin_inff() : (m_run == -__builtin_inff() ? 0.f : m_run);
     float bsum = 0.f;
     f32x16 sa, sb;
     qk_tile(sa, 0);
@@ -308,6 +369,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const AttnArgs a)
         for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(mx, sa[i]);
         __builtin_amdgcn_sched_barrier(0);
       }
+      if (!member) mx = -__builtin_inff();
       const float m_new = __builtin_fmaxf(m_run, pair_max(mx) * sl);
       const float alpha = m_new == m_run ? 1.f : fast_exp2(m_run - m_new);
       l_run *= alpha;
@@ -318,7 +380,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const AttnArgs a)
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         qk_tile(sa, t);
-        probs_tile(sa, pf[2 * t], pf[2 * t + 1], m_run, bsum);
+        probs_tile(sa, pf[2 * t], pf[2 * t + 1], member ? m_run : __builtin_inff(), bsum);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -332,6 +394,11 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const AttnArgs a)
     const int key0 = c * kBlock;
     // valid keys of this block: 0 for an out-of-range index
     const int key_lim = (unsigned)c < (unsigned)R ? (N - key0 < kBlock ? N - key0 : kBlock) : 0;
+
+    // (lanes past the last anchor query are never stored; they keep every
+    // block, as in a plain repeat tile, so they never hold the wave in the
+    // rescale path)
+    if (masked) member = !qvalid || ((bm[qidx * W + (c >> 5)] >> (c & 31)) & 1u);
 
     // ---- K(it) is in LDS once this lane's copies of it have landed and
     // every wave has passed the barrier (V(it) may still be in flight).
@@ -448,7 +515,23 @@ hipError_t launch_v_transpose(const VtArgs& a, hipStream_t stream) {
 
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream) {
   if (a.n_items <= 0) return hipSuccess;
-  hipLaunchKernelGGL(attn_fwd_kernel, dim3(a.n_items), dim3(kThreads), 2 * kTileBytes, stream, a);
+  size_t lds = 2 * kTileBytes;
+  if (a.n_mrep == 0) {
+    hipLaunchKernelGGL(attn_fwd_kernel<false>, dim3(a.n_items), dim3(kThreads), lds, stream, a);
+    return hipGetLastError();
+  }
+  {
+    // masked repeat tiles: bitmaps, union and list behind the two tiles
+    lds += ((size_t)129 * a.mask_words * 4 + 2 * ((size_t)a.n_blocks + 2) + 4 + 15) / 16 * 16;
+    static size_t attr_bytes = 0;
+    if (lds > attr_bytes) {
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_kernel<true>),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      attr_bytes = lds;
+    }
+  }
+  hipLaunchKernelGGL(attn_fwd_kernel<true>, dim3(a.n_items), dim3(kThreads), lds, stream, a);
   return hipGetLastError();
 }
 

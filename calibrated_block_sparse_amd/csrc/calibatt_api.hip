@@ -67,7 +67,7 @@ extern "C" {
 
 const char* calibatt_last_error(void) { return calibatt::g_last_error.c_str(); }
 
-int32_t calibatt_abi_version(void) { return 6; }
+int32_t calibatt_abi_version(void) { return 7; }
 
 
 size_t calibatt_sparse_attn_fwd_workspace(int32_t heads, int32_t n_tokens) {
@@ -91,13 +91,20 @@ static int attn_core(const char* fn, const void* q, const void* k, const void* v
 
   const int32_t R = (int32_t)ceil_div(n_tokens, CALIBATT_BLOCK);
   if ((int64_t)heads * R > 0x7fffffff) return api_fail(CALIBATT_ERR_UNSUPPORTED, "%s: too many tiles", fn);
-  std::vector<int32_t> rep_heads, sparse_heads;
-  for (int32_t h = 0; h < heads; ++h)
-    (repeat_flags && repeat_flags[h] ? rep_heads : sparse_heads).push_back(h);
+  std::vector<int32_t> rep_heads, sparse_heads, masked_heads;
+  for (int32_t h = 0; h < heads; ++h) {
+    const int f = repeat_flags ? repeat_flags[h] : 0;
+    if (f > 2)
+      return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: repeat flag %d of head %d is not 0, 1 or 2", fn, f, h);
+    (f == 0 ? sparse_heads : f == 1 ? rep_heads : masked_heads).push_back(h);
+  }
+  if (!masked_heads.empty() && R > kMaxMaskedRepeatBlocks)
+    return api_fail(CALIBATT_ERR_UNSUPPORTED, "%s: masked repeat heads need R <= %d (R = %d)", fn,
+                    kMaxMaskedRepeatBlocks, R);
 
   AttnArgs a;
   std::memset(&a, 0, sizeof a);
-  if (!rep_heads.empty()) {
+  if (!rep_heads.empty() || !masked_heads.empty()) {
     if (!grid) return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: repeat heads need a grid", fn);
     if (grid->frames <= 0 || grid->rows <= 0 || grid->cols <= 0 ||
         (int64_t)grid->frames * grid->rows * grid->cols != n_tokens)
@@ -112,7 +119,7 @@ static int attn_core(const char* fn, const void* q, const void* k, const void* v
     a.anchors = grid->anchors;
     a.anchor_queries = grid->frames * grid->anchors * grid->cols;
   }
-  if (!sparse_heads.empty() && (!kv_offsets || (!kv_indices && nnz > 0)))
+  if ((!sparse_heads.empty() || !masked_heads.empty()) && (!kv_offsets || (!kv_indices && nnz > 0)))
     return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: null kept-block list", fn);
 
   a.q = static_cast<const uint16_t*>(q);
@@ -129,14 +136,16 @@ static int attn_core(const char* fn, const void* q, const void* k, const void* v
   a.n_blocks = R;
   a.rep_tiles = (int32_t)ceil_div(a.anchor_queries, CALIBATT_BLOCK);
 
-  // Launch in chunks of at most kMaxHeadsPerLaunch heads; repeat heads (the
-  // longest tiles) come first in each launch.
-  size_t ri = 0, si = 0;
-  while (ri < rep_heads.size() || si < sparse_heads.size()) {
+  // Launch in chunks of at most kMaxHeadsPerLaunch heads: masked repeat
+  // heads, plain repeat heads (the longest tiles first), then block-sparse.
+  a.mask_words = (int32_t)ceil_div(R, 32);
+  size_t mi = 0, ri = 0, si = 0;
+  while (mi < masked_heads.size() || ri < rep_heads.size() || si < sparse_heads.size()) {
     int n = 0;
-    a.n_rep = 0;
-    a.n_sparse = 0;
-    while (n < kMaxHeadsPerLaunch && ri < rep_heads.size()) { a.heads[n++] = rep_heads[ri++]; ++a.n_rep; }
+    a.n_mrep = a.n_rep = a.n_sparse = 0;
+    while (n < kMaxHeadsPerLaunch && mi < masked_heads.size()) { a.heads[n++] = masked_heads[mi++]; ++a.n_mrep; }
+    while (n < kMaxHeadsPerLaunch && ri < rep_heads.size()) { a.heads[n++] = rep_heads[ri++]; }
+    a.n_rep = n;
     while (n < kMaxHeadsPerLaunch && si < sparse_heads.size()) { a.heads[n++] = sparse_heads[si++]; ++a.n_sparse; }
     const int64_t items = (int64_t)a.n_rep * a.rep_tiles + (int64_t)a.n_sparse * R;
     if (items > 0x7fffffff) return api_fail(CALIBATT_ERR_UNSUPPORTED, "%s: too many tiles", fn);
@@ -221,7 +230,16 @@ int calibatt_sparse_attn_fwd(const void* q, const void* k, const void* v, void* 
     return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: scale must be finite and > 0", fn);
   if (nnz < 0) return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: nnz < 0", fn);
   bool any_rep = false, any_sparse = false;
-  for (int32_t h = 0; h < heads; ++h) (repeat_flags && repeat_flags[h] ? any_rep : any_sparse) = true;
+  for (int32_t h = 0; h < heads; ++h) {
+    const int f = repeat_flags ? repeat_flags[h] : 0;
+    if (f > 2)
+      return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: repeat flag %d of head %d is not 0, 1 or 2", fn, f, h);
+    if (f == 2 && ceil_div(n_tokens, CALIBATT_BLOCK) > kMaxMaskedRepeatBlocks)
+      return api_fail(CALIBATT_ERR_UNSUPPORTED, "%s: masked repeat heads need R <= %d", fn,
+                      kMaxMaskedRepeatBlocks);
+    (f ? any_rep : any_sparse) = true;
+    if (f == 2) any_sparse = true;  // its lists are read too
+  }
   if (any_rep) {
     if (!grid) return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: repeat heads need a grid", fn);
     if (grid->frames <= 0 || grid->rows <= 0 || grid->cols <= 0 ||

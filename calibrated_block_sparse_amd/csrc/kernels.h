@@ -8,6 +8,7 @@
 namespace calibatt {
 
 constexpr int kMaxHeadsPerLaunch = 256;
+constexpr int kMaxMaskedRepeatBlocks = 896;  // R limit of masked repeat heads (LDS bitmaps)
 
 struct AttnArgs {
   const uint16_t* q;
@@ -24,11 +25,13 @@ struct AttnArgs {
   int32_t n_tokens;
   int32_t n_blocks;
   int32_t n_rep;             // repeat heads in this launch (listed first in heads[])
+  int32_t n_mrep;            // of which masked repeat heads (listed first of all)
   int32_t n_sparse;          // non-repeat heads in this launch
   int32_t rep_tiles;         // query tiles per repeat head
   int32_t n_items;           // n_rep * rep_tiles + n_sparse * n_blocks
   int32_t frames, rows, cols, anchors;
   int32_t anchor_queries;    // frames * anchors * cols
+  int32_t mask_words;        // ceil(R/32): bitmap words of masked repeat tiles
   int32_t heads[kMaxHeadsPerLaunch];
 };
 

@@ -92,7 +92,7 @@ int check_entry(const char* fn, int32_t e, const uint8_t* flags, const int32_t* 
                 int32_t n_tokens) {
   bool any_rep = false;
   for (int32_t h = 0; h < heads; ++h) {
-    if (flags[h] > 1)
+    if (flags[h] > 2)
       return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: entry %d: repeat flag of head %d is %d", fn, e,
                       h, flags[h]);
     any_rep = any_rep || flags[h];

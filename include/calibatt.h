@@ -70,7 +70,7 @@ const char* calibatt_last_error(void);
  * calibatt_prepare_vt and calibatt_sparse_attn_fwd_vt, version 4 the
  * single-pass energy workspace and calibatt_mfma_rate_probe, version 5 the
  * mask bank (calibatt_bank_*) and CALIBATT_ERR_IO, version 6
- * calibatt_spatial_similarity. */
+ * calibatt_spatial_similarity, version 7 masked repeat heads (flag 2). */
 int32_t calibatt_abi_version(void);
 
 /*
@@ -85,11 +85,16 @@ int32_t calibatt_abi_version(void);
  * empty list gets zeros. Lists should be ascending; the order only affects
  * rounding.
  *
- * Repeat head h (repeat_flags[h] != 0; [CalibAtt blog] §二 observation 4,
+ * Repeat head h (repeat_flags[h] == 1; [CalibAtt blog] §二 observation 4,
  * §三): only the `anchors` anchor rows of every frame are computed, densely
  * over all N keys, and each output token (f, y, x) receives the output of
  * query (f, a(y), x), where A(m) = floor((2m+1)*rows / (2*anchors)) and
  * a(y) = A(floor(y*anchors / rows)). Its CSR rows are ignored.
+ *
+ * Masked repeat head (repeat_flags[h] == 2; a variant, the pages name no
+ * mask for repeat heads): as a repeat head, but anchor query n attends only
+ * to the key blocks that its block-row floor(n / 128) keeps in the head's
+ * CSR lists (zeros for a row that keeps nothing). Needs R <= 896.
  *
  *   q, k, v      device bf16 [heads][N][128] (strides as above), inputs
  *   o            device bf16, same layout and strides, output
@@ -100,7 +105,9 @@ int32_t calibatt_abi_version(void);
  *                [0, nnz) and indices outside [0, R) are skipped, so a
  *                malformed list cannot read out of bounds; its result is
  *                unspecified (check lists with calibatt_validate_skiplist).
- *   repeat_flags host uint8 [heads] or NULL (no repeat heads)
+ *   repeat_flags host uint8 [heads] or NULL (no repeat heads): 0 block
+ *                sparse, 1 repeat, 2 masked repeat; other values give
+ *                CALIBATT_ERR_INVALID_ARG
  *   grid         host pointer, required iff a repeat flag is set:
  *                frames*rows*cols == N and 1 <= anchors <= rows
  *   workspace    device, 16-byte aligned, at least
@@ -109,7 +116,7 @@ int32_t calibatt_abi_version(void);
  *                (transposed per key block, zero past N) and the attention
  *                reads V only from there. Its contents after the call are
  *                unspecified; calls sharing one workspace must not overlap.
- * kv_offsets / kv_indices may be NULL when every head repeats.
+ * kv_offsets / kv_indices may be NULL when every head has flag 1.
  * heads == 0 or N == 0 is a no-op. A workspace that is missing, too small or
  * misaligned gives CALIBATT_ERR_WORKSPACE.
  */
@@ -291,7 +298,7 @@ int calibatt_validate_skiplist(const int32_t* kv_offsets, const int32_t* kv_indi
  *   [128, ...)    i32 entry[T][L]
  *   table         E x { i64 payload offset, i64 nnz, u64 FNV-1a-64 of the payload }
  *   payloads      each at a multiple of 256 bytes: u8 repeat_flags[H]
- *                 (0/1), zeros to a multiple of 4, i32 kv_offsets[H*R + 1],
+ *                 (0, 1 or 2), zeros to a multiple of 4, i32 kv_offsets[H*R + 1],
  *                 i32 kv_indices[nnz]; zeros to the next 256 bytes.
  * The file ends at the end of the last padded payload.
  */
@@ -319,7 +326,8 @@ typedef struct calibatt_bank_entry {
  * or NULL (no repeat head; repeat_flags itself may be NULL), kv_offsets[e]
  * int32 [heads*R + 1], kv_indices[e] int32 [kv_offsets[e][heads*R]]. Lists
  * must pass calibatt_validate_skiplist (else CALIBATT_ERR_BAD_SKIPLIST);
- * flags must be 0/1, and any repeat flag needs a grid covering n_tokens.
+ * flags must be 0, 1 or 2 (as for calibatt_sparse_attn_fwd), and any
+ * repeat flag needs a grid covering n_tokens.
  * I/O failures give CALIBATT_ERR_IO.
  */
 int calibatt_bank_write(const char* path, int32_t steps, int32_t layers, int32_t heads,

@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version(lib):
-    assert cbs.calibatt_abi_version() == 6
+    assert cbs.calibatt_abi_version() == 7
 
 
 def fake(n=16):
@@ -90,6 +90,12 @@ def test_attention_argument_errors(lib):
     assert attn(lib, flags=flags, grid=ctypes.byref(g)) == -1
     g = cbs.Grid(2, 16, 32, 17)                                # anchors > rows
     assert attn(lib, flags=flags, grid=ctypes.byref(g)) == -1
+    g = cbs.Grid(2, 16, 32, 5)
+    assert attn(lib, flags=(ctypes.c_uint8 * 2)(0, 3), grid=ctypes.byref(g)) == -1   # flag 3
+    g = cbs.Grid(2, 450, 128, 5)                               # N = 115200: R = 900 > 896
+    big = lambda **kw: attn(lib, n=115200, sh=115200 * 128,
+                            wsb=cbs.calibatt_sparse_attn_fwd_workspace(2, 115200), **kw)
+    assert big(flags=(ctypes.c_uint8 * 2)(0, 2), grid=ctypes.byref(g)) == -2
     # empty problems are no-ops and succeed
     assert attn(lib, heads=0) == 0 and attn(lib, n=0) == 0
 

@@ -163,7 +163,7 @@ def test_writer_rejects_bad_input(tmp_path):
         write_bank(path, 1, 1, H, N, [[1]], [(off, idx, None)])      # entry out of range
     assert ei.value.code == -1
     with pytest.raises(cbs.CalibAttError) as ei:
-        write_bank(path, 1, 1, H, N, [[0]], [(off, idx, np.array([0, 2], np.uint8))])
+        write_bank(path, 1, 1, H, N, [[0]], [(off, idx, np.array([0, 3], np.uint8))])
     assert ei.value.code == -1
     with pytest.raises(cbs.CalibAttError) as ei:                     # repeat head, no grid
         write_bank(path, 1, 1, H, N, [[0]], [(off, idx, np.array([0, 1], np.uint8))])

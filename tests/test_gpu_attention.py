@@ -292,3 +292,64 @@ def test_out_of_range_entries_are_skipped(gpu):
     for h in range(H):
         want = oracle.block_sparse_attention(*(bf16_bits(t[h]) for t in (q, k, v)), 0.1, mask[h])
         assert_attn_close(f64(o[h]), want, f"head {h}")
+
+
+@pytest.mark.parametrize("F,Hs,W,kk", [(2, 30, 7, 5), (3, 12, 40, 3), (1, 8, 100, 2), (2, 10, 13, 10)])
+def test_masked_repeat_heads_small(gpu, F, Hs, W, kk):
+    """Flags 0 / 1 / 2 in one call: block-sparse, repeat, and repeat heads
+    whose anchor queries keep their block-row's list (one block-row keeps
+    nothing, so its anchor queries give zeros)."""
+    N = F * Hs * W
+    H = 4
+    R = n_blocks(N)
+    say(f"case masked repeat grid {F}x{Hs}x{W} k={kk} R={R}")
+    q, k, v = (gaussian_bf16(430 + i, (H, N, 128), std=1.5).to(DEV) for i in range(3))
+    mask = bernoulli_mask(434, H, R, 0.5, diagonal=True)
+    if R > 2:
+        mask[3, 1, :] = 0
+    flags = np.array([0, 1, 2, 2], np.uint8)
+    o, _, _ = run(gpu, q, k, v, mask, 0.09, flags, (F, Hs, W, kk))
+    for h in range(H):
+        qb, kb, vb = (bf16_bits(t[h]) for t in (q, k, v))
+        if flags[h] == 0:
+            want = oracle.block_sparse_attention(qb, kb, vb, 0.09, mask[h])
+        elif flags[h] == 1:
+            want = oracle.repeat_head_attention(qb, kb, vb, 0.09, F, Hs, W, kk)
+        else:
+            want = oracle.repeat_head_attention_masked(qb, kb, vb, 0.09, F, Hs, W, kk, mask[h])
+        assert_attn_close(f64(o[h]), want, f"head {h} flag {flags[h]}")
+    if R > 2:
+        src = oracle.repeat_source_token(np.arange(N), F, Hs, W, kk)
+        assert not f64(o[3])[src // 128 == 1].any()
+
+
+def test_masked_repeat_with_every_block_kept_is_plain_repeat(gpu):
+    F, Hs, W, kk = 2, 30, 13, 5
+    N = F * Hs * W
+    R = n_blocks(N)
+    say("case masked repeat, full mask")
+    q, k, v = (gaussian_bf16(440 + i, (2, N, 128)).to(DEV) for i in range(3))
+    mask = np.ones((2, R, R), np.uint8)
+    o1, _, _ = run(gpu, q, k, v, mask, 0.1, np.array([1, 1], np.uint8), (F, Hs, W, kk))
+    o2, _, _ = run(gpu, q, k, v, mask, 0.1, np.array([2, 2], np.uint8), (F, Hs, W, kk))
+    assert torch.equal(o1, o2)
+
+
+def test_masked_repeat_mochi_shape_sampled(gpu):
+    """Mochi 480p layer with its repeat heads also keeping their masks:
+    sampled tokens of every repeat head against the oracle."""
+    w = ATTN_WORKLOADS["mochi1_480p_layer"]
+    say(f"case masked repeat {w.name}")
+    q, k, v = qkv(w, device=DEV)
+    mask = block_mask(w)
+    flags = repeat_flags(w) * 2
+    grid = (w.grid.frames, w.grid.rows, w.grid.cols, w.anchors)
+    o, _, _ = run(gpu, q, k, v, mask, w.scale, flags, grid)
+    for h in np.flatnonzero(flags):
+        qb, kb, vb = (bf16_bits(t[h]) for t in (q, k, v))
+        rng = np.random.Generator(np.random.PCG64(2000 + h))
+        toks = np.r_[np.arange(64), rng.integers(0, w.n_tokens, 448), w.n_tokens - 1]
+        want = oracle.repeat_head_attention_masked(qb, kb, vb, w.scale, *grid, mask[h], toks)
+        got = f64(o[h][torch.from_numpy(toks).to(DEV)])
+        e = assert_attn_close(got, want, f"masked repeat head {h}")
+    say(f"  last head max-abs {e[0]:.2e}")
