@@ -43,8 +43,7 @@ namespace calibatt {
 // are at most 2^8 and the final division by the row sum cancels the choice
 // of reference exactly, so this saves the rescale of the output accumulator
 // on almost every block without changing the result.
-constexpr float kLazyRescaleLog2 = 8.f;
-constexpr float kLazyRescaleLimit = 256.f;  // 2^kLazyRescaleLog2
+constexpr float kLazyRescaleLimit = 256.f;  // 2^8
 
 // LDS operand reads kept in flight ahead of the MFMA that uses them.
 #ifndef CALIBATT_READ_DEPTH
@@ -120,7 +119,6 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const AttnArgs a)
   const int64_t hoff = (int64_t)head * a.stride_head;
   const uint16_t* __restrict__ qh = a.q + hoff;
   const uint16_t* __restrict__ kh = a.k + hoff;
-  const uint16_t* __restrict__ vh = a.v + hoff;
   uint16_t* __restrict__ oh = a.o + hoff;
 
   // ---- this lane's query row
@@ -238,8 +236,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const AttnArgs a)
   if (beg < end) {
     c = block_at(beg);
     const int cl = (unsigned)c < (unsigned)R ? c : 0;
-    copy_tile<false>(ldsK, kh, cp, cl * kBlock, N, wave, lane);
-    copy_tile<false>(ldsV, vth, cpt, cl * kBlock, R * kBlock, wave, lane);
+    copy_tile(ldsK, kh, cp, cl * kBlock, N, wave, lane);
+    copy_tile(ldsV, vth, cpt, cl * kBlock, R * kBlock, wave, lane);
   }
 
   // S^T tile t (keys 32t .. 32t+31 of the block x this wave's 32 queries).
@@ -335,7 +333,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const AttnArgs a)
   // probabilities. They are computed against the current reference max
   // before anything about this block is known, so the exponentials of tile t
   // overlap the MFMAs of tile t+1. The reference is only moved (lazy
-  // rescale) when some lane's sum exceeds 2^kLazyRescaleLog2 -- which bounds
+  // rescale) when some lane's sum exceeds 2^8 -- which bounds
   // every probability by 2^8 without computing the block max -- or on the
   // first block; then the block max is found, the output rescaled and the
   // block recomputed from the K tile still in LDS.
@@ -413,7 +411,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const AttnArgs a)
     }
     l_run += bsum;
     lds_barrier();  // every wave is done with sK
-    if (has_next) copy_tile<false>(ldsK, kh, cp, cnl * kBlock, N, wave, lane);
+    if (has_next) copy_tile(ldsK, kh, cp, cnl * kBlock, N, wave, lane);
 
     // ---- V(it) in LDS (K(it+1) may still be in flight)
     if (has_next) wait_vmem<kCopiesPerTile>();
@@ -425,7 +423,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const AttnArgs a)
     pv_steps(pf, 4);
     pipeline_reads<16, CALIBATT_READ_DEPTH, 0>();
     lds_barrier();  // every wave is done with sV
-    if (has_next) copy_tile<false>(ldsV, vth, cpt, cnl * kBlock, R * kBlock, wave, lane);
+    if (has_next) copy_tile(ldsV, vth, cpt, cnl * kBlock, R * kBlock, wave, lane);
     c = cn;
   }
 

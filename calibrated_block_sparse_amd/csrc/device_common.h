@@ -25,7 +25,6 @@ namespace calibatt {
 constexpr int kBlock = 128;       // tokens per block (B)
 constexpr int kDim = 128;         // head dimension (D)
 constexpr int kThreads = 256;     // 4 waves
-constexpr int kLdsStride = 136;   // bf16 per LDS tile row: 256 B + 16 B pad
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -56,66 +55,6 @@ __device__ __forceinline__ u32x4 load16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
-// Copies the 128 x 128 key tile starting at token key0 into LDS, row-major
-// with a padded row stride; rows at or past n_tokens are zero.
-__device__ __forceinline__ void stage_rows(uint16_t* __restrict__ lds,
-                                           const uint16_t* __restrict__ src,
-                                           int64_t stride_token, int key0,
-                                           int n_tokens, int tid) {
-  u32x4 buf[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int idx = tid + kThreads * j;
-    const int row = idx >> 4, ch = idx & 15;
-    const bool ok = key0 + row < n_tokens;
-    buf[j] = ok ? load16(src + (int64_t)(key0 + row) * stride_token + ch * 8)
-                : u32x4{0u, 0u, 0u, 0u};
-  }
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int idx = tid + kThreads * j;
-    const int row = idx >> 4, ch = idx & 15;
-    *reinterpret_cast<u32x4*>(lds + row * kLdsStride + ch * 8) = buf[j];
-  }
-}
-
-// Copies the 128 x 128 value tile starting at token key0 into LDS transposed
-// ([d][key]) so that the P.V product can read 8 keys of one d as one 16-byte
-// LDS load. Inside every group of 16 keys the order is
-//   keys 0-3, 8-11, 4-7, 12-15,
-// which puts the 8 keys that MFMA lane group g needs for one k-step
-// (4g..4g+3 and 8+4g..8+4g+3, see attention kernel) side by side.
-// Thread t handles keys 4*(t%32) .. +3 and d range 16*(t/32) .. +15.
-__device__ __forceinline__ void stage_values_transposed(uint16_t* __restrict__ lds,
-                                                        const uint16_t* __restrict__ src,
-                                                        int64_t stride_token, int key0,
-                                                        int n_tokens, int tid) {
-  const int kg = tid & 31, dc = tid >> 5;
-  u32x4 vr[4][2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int key = key0 + 4 * kg + i;
-    const bool ok = key < n_tokens;
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-      vr[i][h] = ok ? load16(src + (int64_t)key * stride_token + 16 * dc + 8 * h)
-                    : u32x4{0u, 0u, 0u, 0u};
-  }
-  const int a = kg & 3;
-  const int pos = (kg >> 2) * 16 + ((a & 1) << 3) + ((a & 2) << 1);
-#pragma unroll
-  for (int dd = 0; dd < 16; ++dd) {
-    const int h = dd >> 3, w = (dd & 7) >> 1;
-    const int sh = (dd & 1) * 16;
-    const uint32_t e0 = (vr[0][h][w] >> sh) & 0xffffu;
-    const uint32_t e1 = (vr[1][h][w] >> sh) & 0xffffu;
-    const uint32_t e2 = (vr[2][h][w] >> sh) & 0xffffu;
-    const uint32_t e3 = (vr[3][h][w] >> sh) & 0xffffu;
-    u32x2 out = {e0 | (e1 << 16), e2 | (e3 << 16)};
-    *reinterpret_cast<u32x2*>(lds + (16 * dc + dd) * kLdsStride + pos) = out;
-  }
-}
-
 // Query fragment (B operand of S^T = K Q^T) for one lane: row `tok` of q,
 // d = 16*s + 8*g .. +7 for s = 0..7. Zero when !valid.
 __device__ __forceinline__ void load_query(bf16x8 (&qf)[8], const uint16_t* __restrict__ q,
@@ -128,37 +67,6 @@ __device__ __forceinline__ void load_query(bf16x8 (&qf)[8], const uint16_t* __re
   }
 }
 
-// S^T for one wave: sacc[t] holds keys 32t..32t+31 (rows) x the wave's 32
-// queries (columns). Keys come from the LDS tile written by stage_rows.
-__device__ __forceinline__ void scores_transposed(f32x16 (&sacc)[4], const uint16_t* __restrict__ sK,
-                                                  const bf16x8 (&qf)[8], int l32, int g) {
-#pragma unroll
-  for (int t = 0; t < 4; ++t) sacc[t] = f32x16{};
-#pragma unroll
-  for (int s = 0; s < 8; ++s) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sK + (32 * t + l32) * kLdsStride + 16 * s + 8 * g);
-      sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[t], 0, 0, 0);
-    }
-  }
-}
-
-// Key (0..127 inside the block) held by accumulator element i of tile t.
-__device__ __forceinline__ int acc_key(int t, int i, int g) {
-  return 32 * t + 8 * (i >> 2) + 4 * g + (i & 3);
-}
-
-// Sets scores of keys at or past n_tokens to -inf (ragged last block).
-__device__ __forceinline__ void mask_ragged_keys(f32x16 (&sacc)[4], int key0, int n_tokens, int g) {
-  if (key0 + kBlock <= n_tokens) return;
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      if (key0 + acc_key(t, i, g) >= n_tokens) sacc[t][i] = -__builtin_inff();
-}
-
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---------------------------------------------------------------------------
@@ -167,8 +75,9 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // A 128 x 128 bf16 tile occupies 32 KiB of LDS: row r (token key0 + r) at
 // byte r*256, its sixteen 16-byte chunks permuted by an XOR swizzle so that
 // the reads the MFMA operands need hit distinct LDS banks:
-//   K tiles: physical chunk = logical chunk ^ (r % 16)   (row-wise ds_read_b128)
-//   V tiles: physical chunk = logical chunk ^ 4*(r % 4)  (ds_read_b64_tr_b16)
+//   physical chunk = logical chunk ^ (r % 16)
+// so the 16-byte operand reads of 16 consecutive rows hit distinct banks
+// (K tiles, and V^T tiles, which take the same path).
 // One global_load_lds_dwordx4 moves 64 lanes x 16 B into 1 KiB of LDS (lane
 // i to byte 16*i of the block M0 points at), i.e. four rows. Wave w copies
 // rows 32w .. 32w+31 with eight such instructions; instruction j covers rows
@@ -184,9 +93,6 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 constexpr int kTileBytes = kBlock * kDim * 2;   // 32 KiB
 constexpr int kCopiesPerTile = 8;               // per wave
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 
@@ -199,14 +105,8 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // otherwise print a vector register the compiler chose to keep it in).
 __device__ __forceinline__ uint32_t uni(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
 
-// 16 bytes per lane from sbase + voff into LDS [lds + 16*lane]. sbase and lds
-// must be wave-uniform.
-__device__ __forceinline__ void copy16_saddr(uint32_t lds, const void* sbase, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :: "s"(uni(lds)), "v"(voff), "s"(sbase) : "memory", "m0");
-}
-
-// Same with a per-lane 64-bit address.
+// 16 bytes per lane from a per-lane 64-bit address into LDS [lds + 16*lane]
+// (lds wave-uniform).
 __device__ __forceinline__ void copy16_vaddr(uint32_t lds, const void* vaddr) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                :: "s"(uni(lds)), "v"(vaddr) : "memory", "m0");
@@ -228,14 +128,13 @@ __device__ __forceinline__ void lds_barrier() {
 
 // Per-lane source offsets of the fast copy path, fixed for the kernel.
 // Instruction j of a wave covers rows 32w + 4j + sub (sub = lane / 16) with
-// physical chunk p = lane % 16. K swizzles chunks by (row % 16) = 4(j%4) + sub:
+// physical chunk p = lane % 16. The swizzle is (row % 16) = 4(j%4) + sub:
 // logical chunk p ^ sub ^ 4(j%4), i.e. the j = 0 offset with bits 6-7 flipped
 // by (j%4) << 6 -- valid while a row's byte offset has zero low 8 bits, so the
 // fast path requires row_bytes % 256 == 0 (other strides take the per-lane
-// path). V swizzles by 4*(row % 4) = 4*sub, the same for every j.
+// path).
 struct CopyPlan {
   uint32_t k_off;      // row sub, chunk p ^ sub
-  uint32_t v_off;      // row sub, chunk p ^ 4*sub
   int64_t row_bytes;   // stride_token * 2
   bool fast;           // row_bytes % 256 == 0
 };
@@ -245,7 +144,6 @@ __device__ __forceinline__ CopyPlan make_copy_plan(int64_t stride_token, int lan
   const int sub = lane >> 4, p = lane & 15;
   cp.row_bytes = stride_token * 2;
   cp.k_off = (uint32_t)(sub * cp.row_bytes + ((p ^ sub) << 4));
-  cp.v_off = (uint32_t)(sub * cp.row_bytes + ((p ^ (sub << 2)) << 4));
   cp.fast = (cp.row_bytes & 255) == 0;
   return cp;
 }
@@ -299,39 +197,12 @@ __device__ __forceinline__ void copy_k_fast(uint32_t lds, u32x4 rs, uint32_t sof
       : "memory", "m0", "scc");
 }
 
-// Eight copies of rows 32*wave .. +31 of a full V tile; the row base
-// advances 4 rows per instruction.
-__device__ __forceinline__ void copy_v_fast(uint32_t lds, u32x4 rs, uint32_t soff, uint32_t step4,
-                                            uint32_t v) {
-  asm volatile(
-      "s_mov_b32 m0, %[lds]\n\ts_nop 0\n\t"
-      "buffer_load_dwordx4 %[v], %[rs], %[so] offen lds\n\t"
-      "s_add_u32 %[so], %[so], %[st]\n\ts_add_u32 m0, m0, 0x400\n\ts_nop 0\n\t"
-      "buffer_load_dwordx4 %[v], %[rs], %[so] offen lds\n\t"
-      "s_add_u32 %[so], %[so], %[st]\n\ts_add_u32 m0, m0, 0x400\n\ts_nop 0\n\t"
-      "buffer_load_dwordx4 %[v], %[rs], %[so] offen lds\n\t"
-      "s_add_u32 %[so], %[so], %[st]\n\ts_add_u32 m0, m0, 0x400\n\ts_nop 0\n\t"
-      "buffer_load_dwordx4 %[v], %[rs], %[so] offen lds\n\t"
-      "s_add_u32 %[so], %[so], %[st]\n\ts_add_u32 m0, m0, 0x400\n\ts_nop 0\n\t"
-      "buffer_load_dwordx4 %[v], %[rs], %[so] offen lds\n\t"
-      "s_add_u32 %[so], %[so], %[st]\n\ts_add_u32 m0, m0, 0x400\n\ts_nop 0\n\t"
-      "buffer_load_dwordx4 %[v], %[rs], %[so] offen lds\n\t"
-      "s_add_u32 %[so], %[so], %[st]\n\ts_add_u32 m0, m0, 0x400\n\ts_nop 0\n\t"
-      "buffer_load_dwordx4 %[v], %[rs], %[so] offen lds\n\t"
-      "s_add_u32 %[so], %[so], %[st]\n\ts_add_u32 m0, m0, 0x400\n\ts_nop 0\n\t"
-      "buffer_load_dwordx4 %[v], %[rs], %[so] offen lds"
-      : [so] "+s"(soff)
-      : [lds] "s"(uni(lds)), [rs] "s"(rs), [st] "s"(uni(step4)), [v] "v"(v)
-      : "memory", "m0", "scc");
-}
-
 #pragma clang diagnostic pop
 
-// Issues this wave's eight copies of the tile whose first token row is key0
-// (kIsV selects the V swizzle). Rows at or past n_tokens are read from row
-// n_tokens - 1 instead (their scores repeat a real score of the block and
-// their probabilities are zeroed, so those values never matter).
-template <bool kIsV>
+// Issues this wave's eight copies of the tile whose first token row is
+// key0. Rows at or past n_tokens are read from row n_tokens - 1 instead
+// (their scores repeat a real score of the block and their probabilities are
+// zeroed, so those values never matter).
 __device__ __forceinline__ void copy_tile(uint32_t lds_tile, const uint16_t* __restrict__ src,
                                           const CopyPlan& cp, int key0, int n_tokens, int wave,
                                           int lane) {
@@ -339,18 +210,15 @@ __device__ __forceinline__ void copy_tile(uint32_t lds_tile, const uint16_t* __r
   if (cp.fast && key0 + kBlock <= n_tokens) {
     const u32x4 rs = make_rsrc(reinterpret_cast<const char*>(src) + (int64_t)key0 * cp.row_bytes);
     const uint32_t soff = uni((uint32_t)(32 * wave) * (uint32_t)cp.row_bytes);
-    if (kIsV)
-      copy_v_fast(lds, rs, soff, 4u * (uint32_t)cp.row_bytes, cp.v_off);
-    else
-      copy_k_fast(lds, rs, soff, 4u * (uint32_t)cp.row_bytes, cp.k_off);
+    copy_k_fast(lds, rs, soff, 4u * (uint32_t)cp.row_bytes, cp.k_off);
   } else {
     const int sub = lane >> 4, p = lane & 15;
 #pragma unroll
     for (int j = 0; j < kCopiesPerTile; ++j) {
       const int row = 32 * wave + 4 * j + sub;
-      const int chunk = kIsV ? (p ^ ((row & 3) << 2)) : (p ^ (row & 15));
       const int tok = key0 + row < n_tokens ? key0 + row : n_tokens - 1;
-      copy16_vaddr(lds + 1024 * j, reinterpret_cast<const char*>(src) + (int64_t)tok * cp.row_bytes + chunk * 16);
+      copy16_vaddr(lds + 1024 * j,
+                   reinterpret_cast<const char*>(src) + (int64_t)tok * cp.row_bytes + (p ^ (row & 15)) * 16);
     }
   }
 }
@@ -361,22 +229,6 @@ __device__ __forceinline__ int k_operand_offset(int row, int s, int g) {
   return row * 256 + ((((2 * s + g) ^ (row & 15))) << 4);
 }
 
-// Transposed read of V for the P.V product. For 16-key group s of the tile
-// and output tile u (d = 32u .. 32u+31), the A operand of lane l holds
-// V[key][32u + l%32] for the eight keys 16s + 4g + {0..3} and
-// 16s + 8 + 4g + {0..3} (g = l/32). ds_read_b64_tr_b16 hands lane i of each
-// 16-lane group element i%4 of the 8 bytes read by lanes 4m + i/4, m = 0..3,
-// so lane (m = (l%16)/4, q = l%4) of group j = l/16 reads the four d values
-// 32u + 16(j%2) + 4q .. +3 of key 16s + 8h + 4(j/2) + m (h = 0, then 1).
-// v_operand_offset gives the swizzled byte offset for s = 0, h = 0; key
-// group s adds s*4096 and h = 1 adds 2048.
-__device__ __forceinline__ int v_operand_offset(int u, int lane) {
-  const int j = lane >> 4, m = (lane >> 2) & 3, q = lane & 3;
-  const int row = 4 * (j >> 1) + m;
-  const int chunk = (4 * u + 2 * (j & 1) + (q >> 1)) ^ (4 * m);
-  return row * 256 + chunk * 16 + (q & 1) * 8;
-}
-
 typedef __attribute__((address_space(3))) const uint8_t* lds_cptr;
 
 // LDS loads at an LDS byte address. Callers pass a per-lane base plus a
@@ -384,21 +236,6 @@ typedef __attribute__((address_space(3))) const uint8_t* lds_cptr;
 // 16-bit offset field (so one base register serves many loads).
 __device__ __forceinline__ bf16x8 lds_read_b128(uint32_t addr) {
   return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>((lds_cptr)(uintptr_t)addr);
-}
-
-__device__ __forceinline__ bf16x8 lds_read_v_operand(uint32_t addr) {
-  typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(uintptr_t)addr);
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(uintptr_t)(addr + 2048));
-  const bf16x4 a = __builtin_bit_cast(bf16x4, lo), b = __builtin_bit_cast(bf16x4, hi);
-  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-__device__ __forceinline__ bf16x8 v_operand(const uint8_t* vtile, int off) {
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(vtile + off));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(vtile + off + 2048));
-  const bf16x4 a = __builtin_bit_cast(bf16x4, lo), b = __builtin_bit_cast(bf16x4, hi);
-  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 }  // namespace calibatt

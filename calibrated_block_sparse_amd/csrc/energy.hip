@@ -87,14 +87,14 @@ __global__ void __launch_bounds__(kThreads, 2) energy_partials_kernel(const Ener
   float m_run = -__builtin_inff();  // integer-valued once set
   float l_run = 0.f;
 
-  copy_tile<false>(lds0, kh, cp, 0, N, wave, lane);
+  copy_tile(lds0, kh, cp, 0, N, wave, lane);
 
   // One block with its K tile in buffer kBuf.
   auto block = [&](auto kBufC, int c) {
     constexpr int kBuf = decltype(kBufC)::value;
     wait_vmem<0>();
     lds_barrier();  // K(c) landed; every wave is done with the other buffer
-    if (c + 1 < R) copy_tile<false>(lds0 + (1 - kBuf) * kTileBytes, kh, cp, (c + 1) * kBlock, N, wave, lane);
+    if (c + 1 < R) copy_tile(lds0 + (1 - kBuf) * kTileBytes, kh, cp, (c + 1) * kBlock, N, wave, lane);
 
     f32x16 sacc[4];
 #pragma unroll
