@@ -14,7 +14,7 @@ with every block kept, the roofline of the kernel (bf16 MFMA peak), the
 other layer shapes and the calibration pass, and the fp64 CPU oracle timed
 on a bounded sample of the same workload.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-extras] [--no-cpu]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--no-extras] [--no-cpu]
 """
 
 from __future__ import annotations
@@ -334,7 +334,7 @@ def traffic_record():
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="wan21_720p_layer")
     ap.add_argument("--no-extras", action="store_true")

@@ -519,15 +519,14 @@ hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream) {
     return hipGetLastError();
   }
   {
-    // masked repeat tiles: bitmaps, union and list behind the two tiles
+    // masked repeat tiles: bitmaps, union and list behind the two tiles.
+    // The dynamic-LDS limit is a per-device attribute of the kernel; it is
+    // set on every such launch (a host-side call), so calls from several
+    // threads or on several devices need no shared state.
     lds += ((size_t)129 * a.mask_words * 4 + 2 * ((size_t)a.n_blocks + 2) + 4 + 15) / 16 * 16;
-    static size_t attr_bytes = 0;
-    if (lds > attr_bytes) {
-      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_kernel<true>),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e != hipSuccess) return e;
-      attr_bytes = lds;
-    }
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_kernel<true>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(attn_fwd_kernel<true>, dim3(a.n_items), dim3(kThreads), lds, stream, a);
   return hipGetLastError();
