@@ -58,6 +58,11 @@ int check_tensor_layout(const char* fn, int32_t heads, int32_t n_tokens, int32_t
     return api_fail(CALIBATT_ERR_INVALID_ARG,
                 "%s: strides (head %lld, token %lld) must be multiples of 8 with token >= %d", fn,
                 (long long)stride_head, (long long)stride_token, head_dim);
+  // the tile copies address the 128 rows of a block with 32-bit byte
+  // offsets from the block's first row
+  if (stride_token > CALIBATT_MAX_STRIDE_TOKEN)
+    return api_fail(CALIBATT_ERR_UNSUPPORTED, "%s: stride_token %lld > %d", fn,
+                    (long long)stride_token, CALIBATT_MAX_STRIDE_TOKEN);
   return CALIBATT_OK;
 }
 

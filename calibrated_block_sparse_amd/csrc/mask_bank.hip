@@ -242,8 +242,14 @@ int calibatt_bank_open(const char* path, calibatt_bank** out) {
                     (long long)h.file_bytes);
   if (fnv1a64(buf.data() + kHeaderBytes, buf.size() - kHeaderBytes) != h.checksum)
     return api_fail(CALIBATT_ERR_IO, "%s: %s: checksum mismatch", fn, path);
+  // a file that passed its checksum but fails a check of its contents is
+  // reported as corrupt (CALIBATT_ERR_IO) with the check's message
+  auto corrupt = [&]() {
+    const std::string why = calibatt_last_error();
+    return api_fail(CALIBATT_ERR_IO, "%s: %s: %s", fn, path, why.c_str());
+  };
   int rc = check_shape(fn, h.steps, h.layers, h.heads, h.n_tokens, h.n_entries);
-  if (rc) return rc;
+  if (rc) return corrupt();
   const int32_t R = (h.n_tokens + CALIBATT_BLOCK - 1) / CALIBATT_BLOCK;
   if (h.n_blocks != R)
     return api_fail(CALIBATT_ERR_IO, "%s: %s: n_blocks %d != ceil(N/128) = %d", fn, path, h.n_blocks, R);
@@ -253,7 +259,7 @@ int calibatt_bank_open(const char* path, calibatt_bank** out) {
     return api_fail(CALIBATT_ERR_IO, "%s: %s: bad entry table offset", fn, path);
   calibatt_grid grid{h.frames, h.rows, h.cols, h.anchors};
   const bool has_grid = h.frames != 0 || h.rows != 0 || h.cols != 0 || h.anchors != 0;
-  if (has_grid && (rc = check_grid(fn, grid, h.n_tokens))) return rc;
+  if (has_grid && check_grid(fn, grid, h.n_tokens)) return corrupt();
 
   auto* b = new calibatt_bank;
   b->hdr = h;
@@ -278,7 +284,7 @@ int calibatt_bank_open(const char* path, calibatt_bank** out) {
     std::memcpy(&sum, t + 16, 8);
     const int64_t bytes = nnz >= 0 && nnz <= (int64_t)h.heads * R * R ? payload_bytes(h.heads, R, nnz) : -1;
     if (bytes < 0 || off % kPayloadAlign || off < h.table_offset + kTableEntryBytes * (int64_t)h.n_entries ||
-        off + bytes > h.file_bytes) {
+        off > h.file_bytes - bytes) {
       delete b;
       return api_fail(CALIBATT_ERR_IO, "%s: %s: entry %d: bad offset or size", fn, path, e);
     }
@@ -296,7 +302,7 @@ int calibatt_bank_open(const char* path, calibatt_bank** out) {
     }
     if ((rc = check_entry(fn, e, flags, kvo, kvi, h.heads, R, has_grid ? &grid : nullptr, h.n_tokens))) {
       delete b;
-      return rc;
+      return rc == CALIBATT_ERR_BAD_SKIPLIST ? rc : corrupt();
     }
     b->payload_offset[e] = off;
     b->nnz[e] = nnz;

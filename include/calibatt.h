@@ -17,7 +17,9 @@
  * - Tensors are bf16 (raw 16-bit storage, passed as void*), laid out as
  *   [heads][N][D] with element strides stride_head and stride_token; D is
  *   contiguous. Base pointers must be 16-byte aligned and both strides
- *   multiples of 8 elements. Batch is folded into heads.
+ *   multiples of 8 elements; stride_token may not exceed
+ *   CALIBATT_MAX_STRIDE_TOKEN (CALIBATT_ERR_UNSUPPORTED). Batch is folded
+ *   into heads.
  * - Every pointer named "device" is device memory owned by the caller. The
  *   library allocates no device memory and keeps no state between calls
  *   except the thread-local error string and the host memory of a mask bank
@@ -51,6 +53,7 @@ enum {
 #define CALIBATT_BLOCK 128
 #define CALIBATT_HEAD_DIM 128
 #define CALIBATT_MAX_BLOCKS 2047 /* R limit of the selection kernels */
+#define CALIBATT_MAX_STRIDE_TOKEN 8388608 /* elements between tokens (2^23) */
 
 /* Latent video grid of a sequence: token n = f*rows*cols + y*cols + x
  * (frame-major, row-major inside a frame; [CalibAtt blog] §六). `anchors`

@@ -79,6 +79,8 @@ def test_attention_argument_errors(lib):
     assert attn(lib, q=None) == -1
     assert attn(lib, q=ctypes.c_void_p(4096 + 2)) == -1
     assert attn(lib, stok=100) == -1
+    assert attn(lib, stok=(1 << 23) + 8) == -2                 # 32-bit tile offsets
+    assert "stride_token" in cbs.calibatt_last_error()
     assert attn(lib, scale=0.0) == -1
     assert attn(lib, scale=float("nan")) == -1
     assert attn(lib, nnz=-1) == -1

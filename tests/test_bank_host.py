@@ -150,6 +150,22 @@ def test_corrupt_files_are_rejected(bank_case, tmp_path):
     assert code(path) == -6
 
 
+def test_header_fields_outside_the_checksum_are_checked(bank_case):
+    """The file checksum covers bytes 128.. only; header fields that
+    contradict the rest are still reported as a corrupt file."""
+    path, (T, L, H, N, grid, entry_of, entries) = bank_case
+    good = open(path, "rb").read()
+    for at, value in ((16, 0),                  # steps = 0
+                      (32, 9),                  # n_blocks != ceil(N / 128)
+                      (36, grid[0] + 1)):       # grid no longer covers N
+        data = bytearray(good)
+        data[at:at + 4] = struct.pack("<i", value)
+        open(path, "wb").write(bytes(data))
+        with pytest.raises(cbs.CalibAttError) as ei:
+            MaskBank(path)
+        assert ei.value.code == -6, (at, value, ei.value)
+
+
 def test_writer_rejects_bad_input(tmp_path):
     H, N = 2, 600
     path = str(tmp_path / "bad.cbsm")
