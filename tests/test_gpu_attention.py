@@ -353,3 +353,29 @@ def test_masked_repeat_mochi_shape_sampled(gpu):
         got = f64(o[h][torch.from_numpy(toks).to(DEV)])
         e = assert_attn_close(got, want, f"masked repeat head {h}")
     say(f"  last head max-abs {e[0]:.2e}")
+
+
+def test_masked_repeat_at_the_block_limit(gpu):
+    """Masked repeat heads at the largest supported R (896 blocks: the
+    per-query bitmaps and the union list fill the LDS left beside the two
+    tiles), one masked repeat head beside a block-sparse head; sampled
+    tokens against the oracle, the block-sparse head on sampled blocks."""
+    F, Hs, W, kk = 28, 32, 128, 5
+    N = F * Hs * W                       # 114,688 tokens = 896 blocks
+    R = n_blocks(N)
+    assert R == 896
+    say(f"case masked repeat at R={R}")
+    q, k, v = (gaussian_bf16(470 + i, (2, N, 128)).to(DEV) for i in range(3))
+    mask = bernoulli_mask(473, 2, R, 0.3, True)
+    flags = np.array([2, 0], np.uint8)
+    o, _, _ = run(gpu, q, k, v, mask, 128 ** -0.5, flags, (F, Hs, W, kk))
+    qb, kb, vb = (bf16_bits(t[0]) for t in (q, k, v))
+    rng = np.random.Generator(np.random.PCG64(474))
+    toks = np.r_[np.arange(32), rng.integers(0, N, 96), N - 1]
+    want = oracle.repeat_head_attention_masked(qb, kb, vb, 128 ** -0.5, F, Hs, W, kk, mask[0], toks)
+    e = assert_attn_close(f64(o[0][torch.from_numpy(toks).to(DEV)]), want, "masked repeat head")
+    blocks = [0, 447, R - 1]
+    want1 = oracle_head_blocks(q, k, v, mask, 128 ** -0.5, 1, blocks)
+    for r, wb in zip(blocks, want1):
+        assert_attn_close(f64(o[1][r * 128:(r + 1) * 128]), wb, f"sparse head block {r}")
+    say(f"  masked head max-abs {e[0]:.2e}")
