@@ -122,6 +122,10 @@ int32_t calibatt_abi_version(void);
  * kv_offsets / kv_indices may be NULL when every head has flag 1.
  * heads == 0 or N == 0 is a no-op. A workspace that is missing, too small or
  * misaligned gives CALIBATT_ERR_WORKSPACE.
+ * The call enqueues kernel launches only (no memset, copy or allocation), so
+ * it can be captured in a HIP graph on `stream`. repeat_flags, grid, heads
+ * and N are read on the host at capture time and fixed in the graph; the
+ * device buffers are read at every replay.
  */
 int calibatt_sparse_attn_fwd(const void* q, const void* k, const void* v, void* o,
                              int32_t heads, int32_t n_tokens, int32_t head_dim,
