@@ -119,9 +119,22 @@ def _check(fn: str, rc: int):
         raise CalibAttError(fn, rc, load_library().calibatt_last_error().decode())
 
 
-def _stream(stream) -> ctypes.c_void_p:
+def _stream(stream, *tensors) -> ctypes.c_void_p:
+    """The stream handle to launch on: `stream`, or the current stream of the
+    device the tensors live on. Every CUDA tensor given must live on that
+    device (the library launches on the stream's device and would otherwise
+    be handed another device's memory)."""
+    devs = {t.device for t in tensors if isinstance(t, torch.Tensor)}
+    for t in tensors:
+        if isinstance(t, torch.Tensor) and not t.is_cuda:
+            raise ValueError(f"expected CUDA tensors, got one on {t.device}")
+    if len(devs) > 1:
+        raise ValueError(f"tensors on different devices: {sorted(str(d) for d in devs)}")
+    dev = next(iter(devs)) if devs else None
     if stream is None:
-        stream = torch.cuda.current_stream()
+        stream = torch.cuda.current_stream(dev)
+    elif dev is not None and stream.device != dev:
+        raise ValueError(f"stream on {stream.device}, tensors on {dev}")
     return ctypes.c_void_p(stream.cuda_stream)
 
 
@@ -189,7 +202,7 @@ def calibatt_sparse_attn_fwd(q, k, v, o, kv_offsets, kv_indices, scale: float,
                                       float(scale), _ptr(kv_offsets), _ptr(kv_indices), nnz,
                                       flags, g, _ptr(workspace),
                                       workspace.numel() * workspace.element_size(),
-                                      _stream(stream))
+                                      _stream(stream, q, k, v, o, kv_offsets, kv_indices, workspace))
     _check("calibatt_sparse_attn_fwd", rc)
 
 
@@ -210,7 +223,7 @@ def calibatt_prepare_vt(v, workspace, stream=None) -> None:
     H, N, D, sh, stok = _attn_layout("calibatt_prepare_vt", v)
     rc = load_library().calibatt_prepare_vt(_ptr(v), H, N, D, sh, stok, _ptr(workspace),
                                             workspace.numel() * workspace.element_size(),
-                                            _stream(stream))
+                                            _stream(stream, v, workspace))
     _check("calibatt_prepare_vt", rc)
 
 
@@ -224,7 +237,8 @@ def calibatt_sparse_attn_fwd_vt(q, k, vt, o, kv_offsets, kv_indices, scale: floa
     rc = load_library().calibatt_sparse_attn_fwd_vt(
         _ptr(q), _ptr(k), _ptr(vt), _ptr(o), H, N, D, sh, stok, float(scale), _ptr(kv_offsets),
         _ptr(kv_indices), nnz, None if flags is None else flags.ctypes.data_as(ctypes.c_void_p),
-        None if g is None else ctypes.byref(g), vt.numel() * vt.element_size(), _stream(stream))
+        None if g is None else ctypes.byref(g), vt.numel() * vt.element_size(),
+        _stream(stream, q, k, vt, o, kv_offsets, kv_indices))
     _check("calibatt_sparse_attn_fwd_vt", rc)
 
 
@@ -246,7 +260,7 @@ def calibatt_block_energy(q, k, energy, scale: float, workspace=None, stream=Non
     rc = load_library().calibatt_block_energy(_ptr(q), _ptr(k), _ptr(energy), H, N, D, sh, stok,
                                               float(scale), _ptr(workspace),
                                               workspace.numel() * workspace.element_size(),
-                                              _stream(stream))
+                                              _stream(stream, q, k, energy, workspace))
     _check("calibatt_block_energy", rc)
 
 
@@ -264,7 +278,8 @@ def calibatt_spatial_similarity(energy_workspace, heads: int, n_tokens: int, gri
     g = Grid(*[int(x) for x in grid])
     rc = load_library().calibatt_spatial_similarity(
         _ptr(energy_workspace), energy_workspace.numel() * energy_workspace.element_size(), heads,
-        n_tokens, ctypes.byref(g), _ptr(row_profiles), _ptr(similarity), _stream(stream))
+        n_tokens, ctypes.byref(g), _ptr(row_profiles), _ptr(similarity),
+        _stream(stream, energy_workspace, row_profiles, similarity))
     _check("calibatt_spatial_similarity", rc)
 
 
@@ -285,7 +300,7 @@ def calibatt_build_mask(energy, eps_fx: int, votes, n_sel=None, stream=None) -> 
     if n_sel is not None and (n_sel.dtype != torch.int32 or n_sel.numel() != D_ * H * R):
         raise ValueError("n_sel must be int32 with n_draws*H*R entries")
     rc = load_library().calibatt_build_mask(_ptr(e), D_, H, R, int(eps_fx), _ptr(votes),
-                                            _ptr(n_sel), _stream(stream))
+                                            _ptr(n_sel), _stream(stream, e, votes, n_sel))
     _check("calibatt_build_mask", rc)
 
 
@@ -298,7 +313,7 @@ def calibatt_finalize_mask(votes, n_prompts: int, rho_num: int, rho_den: int, ma
     rc = load_library().calibatt_finalize_mask(_ptr(votes), H, R, int(n_prompts), int(rho_num),
                                                int(rho_den), _ptr(mask), _ptr(kv_offsets),
                                                _ptr(kv_indices), ctypes.byref(nnz),
-                                               _stream(stream))
+                                               _stream(stream, votes, mask, kv_offsets, kv_indices))
     _check("calibatt_finalize_mask", rc)
     return int(nnz.value)
 
@@ -314,7 +329,7 @@ def calibatt_compile_skiplist(mask, kv_offsets, kv_indices, stream=None) -> int:
     nnz = ctypes.c_int64(0)
     rc = load_library().calibatt_compile_skiplist(_ptr(mask), H, R, _ptr(kv_offsets),
                                                   _ptr(kv_indices), ctypes.byref(nnz),
-                                                  _stream(stream))
+                                                  _stream(stream, mask, kv_offsets, kv_indices))
     _check("calibatt_compile_skiplist", rc)
     return int(nnz.value)
 
@@ -337,7 +352,7 @@ def calibatt_mfma_rate_probe(sink, iters: int, workgroups: int, stream=None) -> 
     (workgroups * 4 waves * iters * 8 MFMAs * 32768)."""
     if sink.dtype != torch.float32 or not sink.is_cuda or sink.numel() < 1:
         raise ValueError("sink must be a CUDA float32 tensor with at least one element")
-    rc = load_library().calibatt_mfma_rate_probe(_ptr(sink), iters, workgroups, _stream(stream))
+    rc = load_library().calibatt_mfma_rate_probe(_ptr(sink), iters, workgroups, _stream(stream, sink))
     _check("calibatt_mfma_rate_probe", rc)
     return int(workgroups) * 4 * int(iters) * 8 * 32768
 

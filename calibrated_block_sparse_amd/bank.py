@@ -112,7 +112,7 @@ class MaskBank:
         shift = (-buf.data_ptr()) % _BANK_ALIGN
         buf = buf[shift:shift + n]
         rc = load_library().calibatt_bank_upload(self._h, ctypes.c_void_p(buf.data_ptr()), n,
-                                                 _stream(stream))
+                                                 _stream(stream, buf))
         _check("calibatt_bank_upload", rc)
         self._buf = buf
         self._views = {}

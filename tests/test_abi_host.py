@@ -8,6 +8,7 @@ import re
 
 import numpy as np
 import pytest
+import torch
 
 import calibrated_block_sparse_amd as cbs
 import oracle
@@ -176,3 +177,10 @@ def test_validate_skiplist_host(lib):
         with pytest.raises(cbs.CalibAttError) as e:
             cbs.calibatt_validate_skiplist(o, i, 3, 9)
         assert e.value.code == -3
+
+
+def test_launch_stream_rejects_host_tensors():
+    # the binding refuses tensors that are not on a GPU before it asks for a
+    # stream or calls the library
+    with pytest.raises(ValueError, match="CUDA"):
+        cbs._stream(None, torch.zeros(4))
