@@ -421,3 +421,19 @@ def test_graph_capture_replays_match_eager(gpu, kind):
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(o, want), f"replay {rep}"
+
+
+@pytest.mark.parametrize("N,H", [(1000, 2), (75600, 1)])
+def test_mask_that_keeps_nothing(gpu, N, H):
+    """Every list empty (nnz = 0, an empty index tensor): the call succeeds
+    and every output row is zero, with the output buffer pre-filled with
+    non-zeros so that unwritten rows would show."""
+    say(f"case empty mask N={N} H={H}")
+    q, k, v = (gaussian_bf16(500 + i, (H, N, 128)).to(DEV) for i in range(3))
+    R = n_blocks(N)
+    off, idx = gpu.compile_skiplist(torch.zeros(H, R, R, dtype=torch.uint8, device=DEV))
+    assert idx.numel() == 0 and not off.any()
+    o = torch.full_like(q, 3.0)
+    gpu.calibatt_sparse_attn_fwd(q, k, v, o, off, idx, 128 ** -0.5)
+    torch.cuda.synchronize()
+    assert not o.float().any()
