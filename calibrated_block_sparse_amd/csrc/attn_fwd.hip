@@ -272,9 +272,9 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const AttnArgs a)
     s0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p_lo, p_lo, 6, 7), ones, s0, false);
     s1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p_hi, p_hi, 6, 7), ones, s1, false);
     bsum += s0 + s1;
-    // Keep these exponentials next to the next tile's MFMAs: without this
-    // use the compiler sinks them past the rescale test (whose rare path
-    // recomputes them), where no MFMA is left to overlap them.
+    // Materialise the probabilities here: left alone the compiler sinks the
+    // exponentials into the branches after the rescale test (whose rare path
+    // recomputes them).
     asm volatile("" ::"v"(p_lo), "v"(p_hi));
   };
 
@@ -329,44 +329,34 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const AttnArgs a)
     }
   };
 
-  // Scores and probabilities of one block; returns this lane's sum of its
-  // probabilities. They are computed against the current reference max
-  // before anything about this block is known, so the exponentials of tile t
-  // overlap the MFMAs of tile t+1. The reference is only moved (lazy
-  // rescale) when some lane's sum exceeds 2^8 -- which bounds
-  // every probability by 2^8 without computing the block max -- or on the
-  // first block; then the block max is found, the output rescaled and the
-  // block recomputed from the K tile still in LDS.
-  auto scores_probs = [&](bf16x8 (&pf)[8]) -> float {
+  // Scores of one block (all four tiles stay in registers, so the K tile is
+  // free, and the next one can be copied, as soon as the last score MFMA
+  // has read it), then its probabilities and this lane's sum of them. The
+  // probabilities are taken against the current reference max before
+  // anything about the block is known; the reference is only moved (lazy
+  // rescale) when some lane's sum exceeds 2^8 -- which bounds every
+  // probability by 2^8 without computing the block max -- or on the first
+  // block; then the block max is taken from the scores in registers, the
+  // output rescaled and the probabilities redone.
+  f32x16 sacc[4];
+  auto scores = [&]() {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) qk_tile(sacc[t], t);
+    pipeline_reads<32, CALIBATT_READ_DEPTH, 0>();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto probs = [&](bf16x8 (&pf)[8]) -> float {
     const float mref = !member ? __builtin_inff() : (m_run == -__builtin_inff() ? 0.f : m_run);
     float bsum = 0.f;
-    f32x16 sa, sb;
-    qk_tile(sa, 0);
-    pipeline_reads<8, CALIBATT_READ_DEPTH, 0>();
-    __builtin_amdgcn_sched_barrier(0);
-    qk_tile(sb, 1);
-    probs_tile(sa, pf[0], pf[1], mref, bsum);
-    pipeline_reads<8, CALIBATT_READ_DEPTH, 6>();
-    __builtin_amdgcn_sched_barrier(0);
-    qk_tile(sa, 2);
-    probs_tile(sb, pf[2], pf[3], mref, bsum);
-    pipeline_reads<8, CALIBATT_READ_DEPTH, 6>();
-    __builtin_amdgcn_sched_barrier(0);
-    qk_tile(sb, 3);
-    probs_tile(sa, pf[4], pf[5], mref, bsum);
-    pipeline_reads<8, CALIBATT_READ_DEPTH, 6>();
-    __builtin_amdgcn_sched_barrier(0);
-    probs_tile(sb, pf[6], pf[7], mref, bsum);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) probs_tile(sacc[t], pf[2 * t], pf[2 * t + 1], mref, bsum);
     const bool first = m_run == -__builtin_inff();
     if (__builtin_amdgcn_ballot_w64(first || bsum > kLazyRescaleLimit)) {
       float mx = -__builtin_inff();
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        qk_tile(sa, t);
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(mx, sa[i]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+        for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(mx, sacc[t][i]);
       if (!member) mx = -__builtin_inff();
       const float m_new = __builtin_fmaxf(m_run, pair_max(mx) * sl);
       const float alpha = m_new == m_run ? 1.f : fast_exp2(m_run - m_new);
@@ -376,11 +366,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const AttnArgs a)
       m_run = m_new;
       bsum = 0.f;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        qk_tile(sa, t);
-        probs_tile(sa, pf[2 * t], pf[2 * t + 1], member ? m_run : __builtin_inff(), bsum);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      for (int t = 0; t < 4; ++t) probs_tile(sacc[t], pf[2 * t], pf[2 * t + 1], member ? m_run : __builtin_inff(), bsum);
     }
     return bsum;
   };
@@ -403,15 +389,16 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const AttnArgs a)
     wait_vmem<kCopiesPerTile>();
     lds_barrier();
 
+    scores();
+    lds_barrier();  // every wave is done with sK: the next K tile copies under the softmax
+    if (has_next) copy_tile(ldsK, kh, cp, cnl * kBlock, N, wave, lane);
     bf16x8 pf[8];
-    float bsum = scores_probs(pf);
+    float bsum = probs(pf);
     if (key_lim < kBlock) {
       zero_masked_probs(pf, key_lim);
       bsum = row_sum(pf);
     }
     l_run += bsum;
-    lds_barrier();  // every wave is done with sK
-    if (has_next) copy_tile(ldsK, kh, cp, cnl * kBlock, N, wave, lane);
 
     // ---- V(it) in LDS (K(it+1) may still be in flight)
     if (has_next) wait_vmem<kCopiesPerTile>();
