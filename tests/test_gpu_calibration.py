@@ -50,19 +50,21 @@ def test_energy_zero_queries_closed_form(gpu):
     np.testing.assert_allclose(e, np.broadcast_to(want, e.shape), rtol=1e-6)
 
 
-def test_energy_calibration_size_sampled(gpu):
-    """Calibration shape (40 heads, N = 32760 = 21 x 30 x 52), one draw,
-    block-rows sampled per head."""
+@pytest.mark.parametrize("part", range(4))
+def test_energy_calibration_size_sampled(gpu, part):
+    """Calibration shape (40 heads, N = 32760 = 21 x 30 x 52), one draw:
+    every head (heads part, part + 4, ... per case) on its first, last and
+    14 seeded block-rows."""
     w = CALIB_WORKLOADS["calibration_480p"]
-    say(f"case energy full-size H={w.heads} N={w.n_tokens}")
+    say(f"case energy full-size part {part}/4 H={w.heads} N={w.n_tokens}")
     basis = calib_basis(w, DEV)
     q, k = calib_draw(w, 0, basis, DEV)
     e = gpu_energy(gpu, q, k, w.scale)
     R = n_blocks(w.n_tokens)
     assert np.allclose(f64(e).sum(axis=-1), 1.0, atol=1e-5)
-    rng = np.random.Generator(np.random.PCG64(7))
-    for h in range(0, w.heads, 4):
-        rows = sorted(set([0, R - 1, *rng.choice(R, 3, replace=False).tolist()]))
+    for h in range(part, w.heads, 4):
+        rng = np.random.Generator(np.random.PCG64(700 + h))
+        rows = sorted(set([0, R - 1, *rng.choice(np.arange(1, R - 1), 14, replace=False).tolist()]))
         want = oracle.block_energy(bf16_bits(q[h]), bf16_bits(k[h]), w.scale, rows)
         assert_energy_close(f64(e[h])[rows], want, f"energy head {h}")
 
