@@ -94,10 +94,24 @@ def block_sparse_attention(q, k, v, scale: float, mask) -> np.ndarray:
 # them to the other rows of the same frame).
 
 
+def check_anchor_geometry(rows: int, anchors: int) -> None:
+    """The repeat head computes its anchor rows and hands each one's output
+    to the other rows of its frame ([CalibAtt blog] §三), so every anchor
+    row must keep its own output: A(m) must lie in the segment m it serves.
+    That holds when anchors == rows or rows >= 2 * anchors - 1; other
+    geometries (rows / 2 < anchors < rows) are rejected."""
+    if not 1 <= anchors <= rows:
+        raise ValueError(f"anchors {anchors} not in [1, rows={rows}]")
+    if anchors != rows and rows < 2 * anchors - 1:
+        raise ValueError(f"{anchors} anchors in {rows} rows: some anchor rows would not serve "
+                         "their own segment")
+
+
 def anchor_rows(rows: int, anchors: int) -> np.ndarray:
     """Evenly spaced anchor rows of a frame with `rows` spatial rows: the
     middle row of each of `anchors` equal segments, A(m) = floor((2m+1) *
     rows / (2 * anchors))."""
+    check_anchor_geometry(rows, anchors)
     m = np.arange(anchors)
     return (2 * m + 1) * rows // (2 * anchors)
 

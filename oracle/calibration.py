@@ -148,11 +148,6 @@ def skiplist_to_mask(offsets, indices, H: int, R: int) -> np.ndarray:
     return m.reshape(H, R, R)
 
 
-def pairs_flop(n_pairs: int, head_dim: int = 128) -> float:
-    """FLOP of n (query block, key block) pairs: 2 GEMMs of B x B x D."""
-    return 4.0 * BLOCK * BLOCK * head_dim * n_pairs
-
-
 __all__ = [n for n in dir() if not n.startswith("_") and n not in ("math", "np")]
 
 

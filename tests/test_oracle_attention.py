@@ -134,6 +134,29 @@ def test_anchor_rows_closed_form():
             assert abs(y - ay) == min(abs(y - b) for b in A)
 
 
+def test_every_anchor_serves_itself_where_supported():
+    """Brute force over small geometries: where the oracle accepts (anchors
+    == rows or rows >= 2 anchors - 1), every anchor row is served by itself
+    and the served rows of each anchor are contiguous; everywhere else the
+    rule would hand some anchor row another anchor's output, and the oracle
+    rejects the geometry."""
+    for Hs in range(1, 41):
+        for k in range(1, Hs + 1):
+            m = np.arange(k)
+            A = (2 * m + 1) * Hs // (2 * k)              # the formula, restated independently
+            a = A[np.arange(Hs) * k // Hs]
+            self_served = all(a[y] == y for y in A)
+            if k == Hs or Hs >= 2 * k - 1:
+                assert self_served, (Hs, k)
+                assert list(oracle.anchor_of_row(Hs, k)) == list(a)
+            else:
+                with pytest.raises(ValueError):
+                    oracle.anchor_rows(Hs, k)
+    # the example of a rejected geometry: 10 rows, 9 anchors (row 1 would copy row 0)
+    with pytest.raises(ValueError):
+        oracle.anchor_of_row(10, 9)
+
+
 def test_repeat_head_reduces_to_dense_when_every_row_is_an_anchor():
     F, Hs, W = 2, 5, 13
     N = F * Hs * W
