@@ -33,6 +33,27 @@ int api_ok() {
   return CALIBATT_OK;
 }
 
+// Anchor A(m) = floor((2m+1) rows / (2k)) serves the rows y with
+// floor(y k / rows) = m. A(m) k / rows >= m + 1/2 - (2k-1)/(2 rows), so A(m)
+// lies in its own segment whenever rows >= 2k - 1 (and trivially when
+// k == rows); for rows/2 < k < rows some anchor rows would receive another
+// anchor's output instead of their own, which the repeat head's broadcast
+// of each anchor to the rest of its frame does not allow.
+int check_grid(const char* fn, const calibatt_grid& g, int32_t n_tokens) {
+  if (g.frames <= 0 || g.rows <= 0 || g.cols <= 0 ||
+      (int64_t)g.frames * g.rows * g.cols != n_tokens)
+    return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: grid %dx%dx%d does not cover N=%d", fn, g.frames,
+                    g.rows, g.cols, n_tokens);
+  if (g.anchors < 1 || g.anchors > g.rows)
+    return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: anchors %d not in [1, rows=%d]", fn, g.anchors,
+                    g.rows);
+  if (g.anchors != g.rows && g.rows < 2 * g.anchors - 1)
+    return api_fail(CALIBATT_ERR_UNSUPPORTED,
+                    "%s: %d anchors in %d rows: needs anchors == rows or rows >= 2*anchors - 1", fn,
+                    g.anchors, g.rows);
+  return CALIBATT_OK;
+}
+
 }  // namespace calibatt
 
 namespace {
@@ -111,13 +132,8 @@ static int attn_core(const char* fn, const void* q, const void* k, const void* v
   std::memset(&a, 0, sizeof a);
   if (!rep_heads.empty() || !masked_heads.empty()) {
     if (!grid) return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: repeat heads need a grid", fn);
-    if (grid->frames <= 0 || grid->rows <= 0 || grid->cols <= 0 ||
-        (int64_t)grid->frames * grid->rows * grid->cols != n_tokens)
-      return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: grid %dx%dx%d does not cover N=%d", fn,
-                  grid->frames, grid->rows, grid->cols, n_tokens);
-    if (grid->anchors < 1 || grid->anchors > grid->rows)
-      return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: anchors %d not in [1, rows=%d]", fn,
-                  grid->anchors, grid->rows);
+    const int grc = check_grid(fn, *grid, n_tokens);
+    if (grc) return grc;
     a.frames = grid->frames;
     a.rows = grid->rows;
     a.cols = grid->cols;
@@ -247,13 +263,8 @@ int calibatt_sparse_attn_fwd(const void* q, const void* k, const void* v, void* 
   }
   if (any_rep) {
     if (!grid) return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: repeat heads need a grid", fn);
-    if (grid->frames <= 0 || grid->rows <= 0 || grid->cols <= 0 ||
-        (int64_t)grid->frames * grid->rows * grid->cols != n_tokens)
-      return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: grid %dx%dx%d does not cover N=%d", fn,
-                  grid->frames, grid->rows, grid->cols, n_tokens);
-    if (grid->anchors < 1 || grid->anchors > grid->rows)
-      return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: anchors %d not in [1, rows=%d]", fn,
-                  grid->anchors, grid->rows);
+    const int grc = check_grid(fn, *grid, n_tokens);
+    if (grc) return grc;
   }
   if (any_sparse && (!kv_offsets || (!kv_indices && nnz > 0)))
     return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: null kept-block list", fn);
@@ -320,13 +331,8 @@ int calibatt_spatial_similarity(const void* energy_workspace, size_t workspace_b
                     heads, n_tokens);
   if (heads == 0 || n_tokens == 0) return api_ok();
   if (!grid) return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: null grid", fn);
-  if (grid->frames <= 0 || grid->rows <= 0 || grid->cols <= 0 ||
-      (int64_t)grid->frames * grid->rows * grid->cols != n_tokens)
-    return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: grid %dx%dx%d does not cover N=%d", fn,
-                    grid->frames, grid->rows, grid->cols, n_tokens);
-  if (grid->anchors < 1 || grid->anchors > grid->rows)
-    return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: anchors %d not in [1, rows=%d]", fn,
-                    grid->anchors, grid->rows);
+  const int grc = check_grid(fn, *grid, n_tokens);
+  if (grc) return grc;
   if (grid->cols > 8192)
     return api_fail(CALIBATT_ERR_UNSUPPORTED, "%s: %d columns > 8192", fn, grid->cols);
   const int64_t R = ceil_div(n_tokens, CALIBATT_BLOCK);
@@ -449,6 +455,13 @@ int calibatt_validate_skiplist(const int32_t* kv_offsets, const int32_t* kv_indi
   if (kv_offsets[rows] != nnz)
     return api_fail(CALIBATT_ERR_BAD_SKIPLIST, "%s: offsets[%lld] = %d != nnz %lld", fn,
                 (long long)rows, kv_offsets[rows], (long long)nnz);
+  // Every offset must lie in [0, nnz] before any index is read: offsets such
+  // as [0, R, 0] pass the end checks but would send row 0 past the array.
+  for (int64_t r = 1; r < rows; ++r) {
+    if (kv_offsets[r] < 0 || kv_offsets[r] > nnz)
+      return api_fail(CALIBATT_ERR_BAD_SKIPLIST, "%s: offsets[%lld] = %d outside [0, nnz = %lld]",
+                      fn, (long long)r, kv_offsets[r], (long long)nnz);
+  }
   for (int64_t r = 0; r < rows; ++r) {
     const int32_t b = kv_offsets[r], e = kv_offsets[r + 1];
     if (e < b) return api_fail(CALIBATT_ERR_BAD_SKIPLIST, "%s: row %lld: offsets decrease", fn, (long long)r);

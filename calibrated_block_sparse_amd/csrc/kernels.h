@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/calibatt.h"
+
 namespace calibatt {
 
 constexpr int kMaxHeadsPerLaunch = 256;
@@ -71,6 +73,11 @@ struct SimArgs {
 // Error reporting of the C ABI (thread-local message, returned status).
 int api_fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 int api_ok();
+
+// Checks a video grid for repeat heads and the similarity score: it covers
+// n_tokens, 1 <= anchors <= rows, and every anchor row lies in the segment
+// it serves (anchors == rows or rows >= 2 * anchors - 1).
+int check_grid(const char* fn, const calibatt_grid& g, int32_t n_tokens);
 
 hipError_t launch_v_transpose(const VtArgs& a, hipStream_t stream);
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream);

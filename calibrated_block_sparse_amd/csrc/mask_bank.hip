@@ -21,6 +21,7 @@
 
 using calibatt::api_fail;
 using calibatt::api_ok;
+using calibatt::check_grid;
 
 namespace {
 
@@ -73,17 +74,6 @@ int check_shape(const char* fn, int32_t steps, int32_t layers, int32_t heads, in
   const int64_t R = (n_tokens + CALIBATT_BLOCK - 1) / CALIBATT_BLOCK;
   if ((int64_t)heads * R * R >= (int64_t)1 << 31 || (int64_t)steps * layers >= (int64_t)1 << 28)
     return api_fail(CALIBATT_ERR_UNSUPPORTED, "%s: bank too large", fn);
-  return CALIBATT_OK;
-}
-
-int check_grid(const char* fn, const calibatt_grid& g, int32_t n_tokens) {
-  if (g.frames <= 0 || g.rows <= 0 || g.cols <= 0 ||
-      (int64_t)g.frames * g.rows * g.cols != n_tokens)
-    return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: grid %dx%dx%d does not cover N=%d", fn, g.frames,
-                    g.rows, g.cols, n_tokens);
-  if (g.anchors < 1 || g.anchors > g.rows)
-    return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: anchors %d not in [1, rows=%d]", fn, g.anchors,
-                    g.rows);
   return CALIBATT_OK;
 }
 

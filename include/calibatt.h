@@ -113,6 +113,10 @@ int32_t calibatt_abi_version(void);
  *                CALIBATT_ERR_INVALID_ARG
  *   grid         host pointer, required iff a repeat flag is set:
  *                frames*rows*cols == N and 1 <= anchors <= rows
+ *                (CALIBATT_ERR_INVALID_ARG otherwise); anchors == rows or
+ *                rows >= 2*anchors - 1, so that every anchor row lies in
+ *                the segment it serves and keeps its own output
+ *                (CALIBATT_ERR_UNSUPPORTED otherwise)
  *   workspace    device, 16-byte aligned, at least
  *                calibatt_sparse_attn_fwd_workspace(heads, N) bytes; the call
  *                first writes V there as [heads][R][128 d][128 keys] tiles
@@ -207,7 +211,9 @@ int calibatt_block_energy(const void* q, const void* k, float* energy,
  * gamma are the caller's.
  *
  *   energy_workspace  device, as filled by calibatt_block_energy
- *   grid              frames*rows*cols == N, 1 <= anchors <= rows, cols <= 8192
+ *   grid              frames*rows*cols == N, 1 <= anchors <= rows, cols <= 8192,
+ *                     anchors == rows or rows >= 2*anchors - 1 (as for
+ *                     calibatt_sparse_attn_fwd)
  *   row_profiles      device fp32 [heads][frames*rows][R], output
  *   similarity        device fp32 [heads], output
  */
@@ -334,7 +340,8 @@ typedef struct calibatt_bank_entry {
  * int32 [heads*R + 1], kv_indices[e] int32 [kv_offsets[e][heads*R]]. Lists
  * must pass calibatt_validate_skiplist (else CALIBATT_ERR_BAD_SKIPLIST);
  * flags must be 0, 1 or 2 (as for calibatt_sparse_attn_fwd), and any
- * repeat flag needs a grid covering n_tokens.
+ * repeat flag needs a grid covering n_tokens (anchor rules as for
+ * calibatt_sparse_attn_fwd).
  * I/O failures give CALIBATT_ERR_IO.
  */
 int calibatt_bank_write(const char* path, int32_t steps, int32_t layers, int32_t heads,

@@ -93,6 +93,9 @@ def test_attention_argument_errors(lib):
     assert attn(lib, flags=flags, grid=ctypes.byref(g)) == -1
     g = cbs.Grid(2, 16, 32, 17)                                # anchors > rows
     assert attn(lib, flags=flags, grid=ctypes.byref(g)) == -1
+    g = cbs.Grid(2, 16, 32, 9)                                 # 16 < 2*9 - 1: anchors off their segments
+    assert attn(lib, flags=flags, grid=ctypes.byref(g)) == -2
+    assert "anchors" in cbs.calibatt_last_error()
     g = cbs.Grid(2, 16, 32, 5)
     assert attn(lib, flags=(ctypes.c_uint8 * 2)(0, 3), grid=ctypes.byref(g)) == -1   # flag 3
     g = cbs.Grid(2, 450, 128, 5)                               # N = 115200: R = 900 > 896
@@ -136,6 +139,7 @@ def test_similarity_argument_errors(lib):
     assert f(g=None) == -1
     assert f(g=ctypes.byref(cbs.Grid(2, 20, 24, 5))) == -1          # does not cover N
     assert f(g=ctypes.byref(cbs.Grid(2, 20, 25, 21))) == -1         # anchors > rows
+    assert f(g=ctypes.byref(cbs.Grid(2, 20, 25, 19))) == -2         # anchors = rows - 1
     assert f(prof=None) == -1
     assert f(wsb=ws - 1) == -4
     assert f(ws=None) == -4
@@ -177,6 +181,28 @@ def test_validate_skiplist_host(lib):
         with pytest.raises(cbs.CalibAttError) as e:
             cbs.calibatt_validate_skiplist(o, i, 3, 9)
         assert e.value.code == -3
+
+
+def test_validate_skiplist_offsets_past_nnz(lib):
+    """Offsets that rise past nnz and fall back (first row [0, R), nnz = 0)
+    pass the checks on offsets[0], offsets[rows] and row 0's length; the
+    validator must reject them before it reads any index."""
+    R = 9
+    off = np.zeros(2 * R + 1, np.int32)
+    off[1] = R                                                 # [0, R, 0, ..., 0], nnz = 0
+    with pytest.raises(cbs.CalibAttError) as e:
+        cbs.calibatt_validate_skiplist(off, np.zeros(0, np.int32), 2, R)
+    assert e.value.code == -3 and "outside" in str(e.value)
+    # the same through the raw C entry point with a NULL index array (legal for nnz = 0)
+    assert lib.calibatt_validate_skiplist(off.ctypes.data_as(ctypes.c_void_p), None, 0, 2, R) == -3
+    # an offset past nnz in the middle of otherwise valid lists
+    m = np.ones((1, R, R), np.uint8)
+    o2, i2 = oracle.compile_skiplist(m)
+    o2 = o2.copy()
+    o2[4] = i2.size + 5
+    with pytest.raises(cbs.CalibAttError) as e:
+        cbs.calibatt_validate_skiplist(o2, i2, 1, R)
+    assert e.value.code == -3
 
 
 def test_launch_stream_rejects_host_tensors():

@@ -166,6 +166,23 @@ def test_header_fields_outside_the_checksum_are_checked(bank_case):
         assert ei.value.code == -6, (at, value, ei.value)
 
 
+def test_offsets_past_nnz_in_a_checksummed_file(tmp_path):
+    """A bank whose lists have offsets rising past nnz and falling back
+    ([0, R, 0, ...] with nnz = 0), written with correct checksums (anyone
+    can recompute them), is rejected as a malformed list before any index
+    is read."""
+    H, N = 2, 1000
+    R = cbs.n_blocks(N)
+    off = np.zeros(H * R + 1, np.int32)
+    off[1] = R
+    entries = [(off, np.zeros(0, np.int32), None)]
+    path = str(tmp_path / "crafted.cbsm")
+    open(path, "wb").write(expected_bytes(1, 1, H, N, None, [[0]], entries))
+    with pytest.raises(cbs.CalibAttError) as ei:
+        MaskBank(path)
+    assert ei.value.code == -3
+
+
 def test_writer_rejects_bad_input(tmp_path):
     H, N = 2, 600
     path = str(tmp_path / "bad.cbsm")
@@ -187,6 +204,10 @@ def test_writer_rejects_bad_input(tmp_path):
     with pytest.raises(cbs.CalibAttError) as ei:                     # grid not covering N
         write_bank(path, 1, 1, H, N, [[0]], [(off, idx, None)], grid=(2, 10, 10, 5))
     assert ei.value.code == -1
+    with pytest.raises(cbs.CalibAttError) as ei:                     # anchors off their segments
+        write_bank(path, 1, 1, H, N, [[0]], [(off, idx, np.array([0, 1], np.uint8))],
+                   grid=(2, 10, 30, 9))
+    assert ei.value.code == -2
     assert not os.path.exists(path) and not os.path.exists(path + ".tmp")
 
 
@@ -208,5 +229,8 @@ def test_custom_op_fake_shape():
     q = torch.empty(2, 300, 128, dtype=torch.bfloat16, device="meta")
     off = torch.empty(2 * 3 + 1, dtype=torch.int32, device="meta")
     idx = torch.empty(5, dtype=torch.int32, device="meta")
-    o = torch.ops.calibatt.sparse_attn(q, q, q, off, idx, None, None, 0.1)
+    o = torch.ops.calibatt.sparse_attn(q, q, q, off, idx, None, None, 0.1, None)
     assert o.shape == q.shape and o.dtype == q.dtype and o.device.type == "meta"
+    ws = torch.empty(2 * 3 * 128 * 128 * 2, dtype=torch.uint8, device="meta")
+    o = torch.ops.calibatt.sparse_attn(q, q, q, off, idx, None, None, 0.1, ws)
+    assert o.shape == q.shape
