@@ -119,8 +119,8 @@ def _check(fn: str, rc: int):
         raise CalibAttError(fn, rc, load_library().calibatt_last_error().decode())
 
 
-def _stream(stream, *tensors) -> ctypes.c_void_p:
-    """The stream handle to launch on: `stream`, or the current stream of the
+def _launch_stream(stream, *tensors) -> "torch.cuda.Stream":
+    """The torch stream to launch on: `stream`, or the current stream of the
     device the tensors live on. Every CUDA tensor given must live on that
     device (the library launches on the stream's device and would otherwise
     be handed another device's memory)."""
@@ -135,7 +135,21 @@ def _stream(stream, *tensors) -> ctypes.c_void_p:
         stream = torch.cuda.current_stream(dev)
     elif dev is not None and stream.device != dev:
         raise ValueError(f"stream on {stream.device}, tensors on {dev}")
-    return ctypes.c_void_p(stream.cuda_stream)
+    return stream
+
+
+def _stream(stream, *tensors) -> ctypes.c_void_p:
+    """The stream handle to launch on (see _launch_stream)."""
+    return ctypes.c_void_p(_launch_stream(stream, *tensors).cuda_stream)
+
+
+def _empty_on(stream, *shape, dtype, device) -> torch.Tensor:
+    """torch.empty allocated on `stream` (a torch stream): the caching
+    allocator then hands the memory to another allocation only after the
+    work enqueued on that stream, so a scratch buffer freed when the binding
+    returns stays valid for the kernels still running on it."""
+    with torch.cuda.stream(stream):
+        return torch.empty(*shape, dtype=dtype, device=device)
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -181,29 +195,34 @@ def calibatt_sparse_attn_fwd(q, k, v, o, kv_offsets, kv_indices, scale: float,
     calibatt_sparse_attn_fwd_workspace bytes (allocated here through torch
     when None)."""
     H, N, D, sh, stok = _attn_layout("calibatt_sparse_attn_fwd", q, k, v, o)
+    nnz = _check_lists(H, N, kv_offsets, kv_indices)
+    flags, g = _flags_grid(H, repeat_flags, grid)
+    lib = load_library()
+    st = _launch_stream(stream, q, k, v, o, kv_offsets, kv_indices, workspace)
+    if workspace is None:
+        need = calibatt_sparse_attn_fwd_workspace(H, N)
+        workspace = _empty_on(st, max(need, 16), dtype=torch.uint8, device=q.device)
+    rc = lib.calibatt_sparse_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), H, N, D, sh, stok,
+                                      float(scale), _ptr(kv_offsets), _ptr(kv_indices), nnz,
+                                      None if flags is None else flags.ctypes.data_as(ctypes.c_void_p),
+                                      None if g is None else ctypes.byref(g), _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(),
+                                      ctypes.c_void_p(st.cuda_stream))
+    _check("calibatt_sparse_attn_fwd", rc)
+
+
+def _check_lists(H: int, N: int, kv_offsets, kv_indices) -> int:
+    """Kept-block lists as the kernels read them: contiguous int32 CUDA
+    tensors, kv_offsets with at least H*R+1 entries. Returns nnz (the
+    length of kv_indices). Either may be None (the library then requires
+    every head to be a plain repeat head)."""
     for t in (kv_offsets, kv_indices):
         if t is not None and (t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous()):
             raise ValueError("kept-block lists must be contiguous int32 CUDA tensors")
-    nnz = 0 if kv_indices is None else kv_indices.numel()
-    flags = None
-    if repeat_flags is not None:
-        arr = np.ascontiguousarray(np.asarray(repeat_flags, dtype=np.uint8))
-        if arr.shape != (H,):
-            raise ValueError("repeat_flags must have one entry per head")
-        flags = arr.ctypes.data_as(ctypes.c_void_p)
-    g = None
-    if grid is not None:
-        g = ctypes.byref(Grid(*[int(x) for x in grid]))
-    lib = load_library()
-    if workspace is None:
-        need = calibatt_sparse_attn_fwd_workspace(H, N)
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    rc = lib.calibatt_sparse_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), H, N, D, sh, stok,
-                                      float(scale), _ptr(kv_offsets), _ptr(kv_indices), nnz,
-                                      flags, g, _ptr(workspace),
-                                      workspace.numel() * workspace.element_size(),
-                                      _stream(stream, q, k, v, o, kv_offsets, kv_indices, workspace))
-    _check("calibatt_sparse_attn_fwd", rc)
+    if kv_offsets is not None and kv_offsets.numel() < H * n_blocks(N) + 1:
+        raise ValueError(f"kv_offsets needs H*R+1 = {H * n_blocks(N) + 1} entries, "
+                         f"has {kv_offsets.numel()}")
+    return 0 if kv_indices is None else kv_indices.numel()
 
 
 def _flags_grid(H, repeat_flags, grid):
@@ -232,7 +251,7 @@ def calibatt_sparse_attn_fwd_vt(q, k, vt, o, kv_offsets, kv_indices, scale: floa
     """o <- block-sparse attention of q, k and the V^T tiles in vt (filled by
     calibatt_prepare_vt); otherwise as calibatt_sparse_attn_fwd."""
     H, N, D, sh, stok = _attn_layout("calibatt_sparse_attn_fwd_vt", q, k, o)
-    nnz = 0 if kv_indices is None else kv_indices.numel()
+    nnz = _check_lists(H, N, kv_offsets, kv_indices)
     flags, g = _flags_grid(H, repeat_flags, grid)
     rc = load_library().calibatt_sparse_attn_fwd_vt(
         _ptr(q), _ptr(k), _ptr(vt), _ptr(o), H, N, D, sh, stok, float(scale), _ptr(kv_offsets),
@@ -255,12 +274,13 @@ def calibatt_block_energy(q, k, energy, scale: float, workspace=None, stream=Non
     if energy.dtype != torch.float32 or not energy.is_contiguous() or energy.shape != (H, R, R):
         raise ValueError("energy must be a contiguous fp32 tensor [H][R][R]")
     need = calibatt_block_energy_workspace(H, N)
+    st = _launch_stream(stream, q, k, energy, workspace)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        workspace = _empty_on(st, max(need, 1), dtype=torch.uint8, device=q.device)
     rc = load_library().calibatt_block_energy(_ptr(q), _ptr(k), _ptr(energy), H, N, D, sh, stok,
                                               float(scale), _ptr(workspace),
                                               workspace.numel() * workspace.element_size(),
-                                              _stream(stream, q, k, energy, workspace))
+                                              ctypes.c_void_p(st.cuda_stream))
     _check("calibatt_block_energy", rc)
 
 
@@ -308,7 +328,17 @@ def calibatt_finalize_mask(votes, n_prompts: int, rho_num: int, rho_den: int, ma
                            kv_offsets, kv_indices, stream=None) -> int:
     """Binarise votes at rho = rho_num/rho_den into mask and compile the
     kept-block lists; returns nnz (waits for the stream)."""
+    if votes.dtype != torch.uint8 or votes.dim() != 3 or votes.shape[1] != votes.shape[2] or \
+            not votes.is_contiguous():
+        raise ValueError("votes must be contiguous uint8 [H][R][R]")
     H, R, _ = votes.shape
+    if mask.dtype != torch.uint8 or mask.shape != votes.shape or not mask.is_contiguous():
+        raise ValueError("mask must be contiguous uint8 with the shape of votes")
+    for t in (kv_offsets, kv_indices):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError("kv_offsets and kv_indices must be contiguous int32 tensors")
+    if kv_offsets.numel() < H * R + 1 or kv_indices.numel() < H * R * R:
+        raise ValueError("kv_offsets needs H*R+1 entries and kv_indices H*R*R")
     nnz = ctypes.c_int64(0)
     rc = load_library().calibatt_finalize_mask(_ptr(votes), H, R, int(n_prompts), int(rho_num),
                                                int(rho_den), _ptr(mask), _ptr(kv_offsets),
@@ -324,6 +354,9 @@ def calibatt_compile_skiplist(mask, kv_offsets, kv_indices, stream=None) -> int:
     H, R, R2 = mask.shape
     if mask.dtype != torch.uint8 or R != R2 or not mask.is_contiguous():
         raise ValueError("mask must be contiguous uint8 [H][R][R]")
+    for t in (kv_offsets, kv_indices):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError("kv_offsets and kv_indices must be contiguous int32 tensors")
     if kv_offsets.numel() < H * R + 1 or kv_indices.numel() < H * R * R:
         raise ValueError("kv_offsets needs H*R+1 entries and kv_indices H*R*R")
     nnz = ctypes.c_int64(0)
@@ -361,19 +394,26 @@ def calibatt_mfma_rate_probe(sink, iters: int, workgroups: int, stream=None) -> 
 # Allocating conveniences (torch allocations + the calls above)
 
 
+# Results and scratch buffers are allocated on the stream the work is
+# enqueued on (the current stream unless `stream` is given).
+
+
 def compile_skiplist(mask: torch.Tensor, stream=None):
     """(kv_offsets, kv_indices[:nnz]) on mask's device."""
     H, R, _ = mask.shape
-    off = torch.empty(H * R + 1, dtype=torch.int32, device=mask.device)
-    idx = torch.empty(max(H * R * R, 1), dtype=torch.int32, device=mask.device)
-    nnz = calibatt_compile_skiplist(mask, off, idx, stream)
+    st = _launch_stream(stream, mask)
+    off = _empty_on(st, H * R + 1, dtype=torch.int32, device=mask.device)
+    idx = _empty_on(st, max(H * R * R, 1), dtype=torch.int32, device=mask.device)
+    nnz = calibatt_compile_skiplist(mask, off, idx, st)
     return off, idx[:nnz]
 
 
 def sparse_attention(q, k, v, kv_offsets, kv_indices, scale: float, repeat_flags=None,
                      grid=None, stream=None) -> torch.Tensor:
-    o = torch.empty_like(q)
-    calibatt_sparse_attn_fwd(q, k, v, o, kv_offsets, kv_indices, scale, repeat_flags, grid, stream)
+    st = _launch_stream(stream, q)
+    with torch.cuda.stream(st):
+        o = torch.empty_like(q)
+    calibatt_sparse_attn_fwd(q, k, v, o, kv_offsets, kv_indices, scale, repeat_flags, grid, st)
     return o
 
 
@@ -382,18 +422,21 @@ def energy_and_similarity(q, k, scale: float, grid, stream=None):
     [H][frames*rows][R]) of q, k for grid (frames, rows, cols, anchors)."""
     H, N, _ = q.shape
     R = n_blocks(N)
-    e = torch.empty(H, R, R, dtype=torch.float32, device=q.device)
-    ws = torch.empty(max(calibatt_block_energy_workspace(H, N), 8), dtype=torch.uint8, device=q.device)
-    calibatt_block_energy(q, k, e, scale, ws, stream)
-    prof = torch.empty(H, grid[0] * grid[1], R, dtype=torch.float32, device=q.device)
-    sim = torch.empty(H, dtype=torch.float32, device=q.device)
-    calibatt_spatial_similarity(ws, H, N, grid, prof, sim, stream)
+    st = _launch_stream(stream, q, k)
+    e = _empty_on(st, H, R, R, dtype=torch.float32, device=q.device)
+    ws = _empty_on(st, max(calibatt_block_energy_workspace(H, N), 8), dtype=torch.uint8,
+                   device=q.device)
+    calibatt_block_energy(q, k, e, scale, ws, st)
+    prof = _empty_on(st, H, grid[0] * grid[1], R, dtype=torch.float32, device=q.device)
+    sim = _empty_on(st, H, dtype=torch.float32, device=q.device)
+    calibatt_spatial_similarity(ws, H, N, grid, prof, sim, st)
     return e, sim, prof
 
 
 def block_energy(q, k, scale: float, stream=None) -> torch.Tensor:
     H, N, _ = q.shape
     R = n_blocks(N)
-    e = torch.empty(H, R, R, dtype=torch.float32, device=q.device)
-    calibatt_block_energy(q, k, e, scale, None, stream)
+    st = _launch_stream(stream, q, k)
+    e = _empty_on(st, H, R, R, dtype=torch.float32, device=q.device)
+    calibatt_block_energy(q, k, e, scale, None, st)
     return e

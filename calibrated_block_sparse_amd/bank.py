@@ -165,20 +165,25 @@ class MaskBank:
 # torch custom op and module
 
 
-@torch.library.custom_op("calibatt::sparse_attn", mutates_args=())
+@torch.library.custom_op("calibatt::sparse_attn", mutates_args=("workspace",))
 def sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_offsets: torch.Tensor,
                 kv_indices: torch.Tensor, repeat_flags: Optional[torch.Tensor],
-                grid: Optional[List[int]], scale: float) -> torch.Tensor:
+                grid: Optional[List[int]], scale: float,
+                workspace: Optional[torch.Tensor]) -> torch.Tensor:
     """Block-sparse attention with repeat heads (calibatt_sparse_attn_fwd);
-    repeat_flags is a host uint8 tensor [H] or None."""
+    repeat_flags is a host uint8 tensor [H] or None. workspace: a uint8 CUDA
+    tensor of calibatt_sparse_attn_fwd_workspace(H, N) bytes kept by the
+    caller across calls (its contents are scratch), or None to have one
+    allocated for this call."""
     o = torch.empty_like(q)
     flags = None if repeat_flags is None else repeat_flags.cpu().numpy()
-    calibatt_sparse_attn_fwd(q, k, v, o, kv_offsets, kv_indices, scale, flags, grid)
+    calibatt_sparse_attn_fwd(q, k, v, o, kv_offsets, kv_indices, scale, flags, grid,
+                             workspace=workspace)
     return o
 
 
 @sparse_attn.register_fake
-def _sparse_attn_fake(q, k, v, kv_offsets, kv_indices, repeat_flags, grid, scale):
+def _sparse_attn_fake(q, k, v, kv_offsets, kv_indices, repeat_flags, grid, scale, workspace):
     return torch.empty_like(q)
 
 
@@ -186,13 +191,33 @@ class CalibAttention(torch.nn.Module):
     """Attention of one DiT layer with the calibrated masks of a bank: the
     call for (t, l) fetches that entry's lists and repeat flags (no run-time
     decision) and runs calibatt::sparse_attn. q, k, v: [H][N][128] bf16 on
-    the bank's device."""
+    the bank's device.
 
-    def __init__(self, bank: MaskBank, scale: Optional[float] = None):
+    The module keeps one V^T workspace (calibatt_sparse_attn_fwd_workspace
+    bytes: 775 MB for 40 heads at N = 75600) for all its calls, allocated on
+    the first call for a given (H, N, device); calls of one module therefore
+    must not run concurrently on different streams. `workspace` passes a
+    caller-owned buffer instead."""
+
+    def __init__(self, bank: MaskBank, scale: Optional[float] = None,
+                 workspace: Optional[torch.Tensor] = None):
         super().__init__()
         self.bank = bank
         self.scale = scale if scale is not None else 128 ** -0.5
         self._flags = {}
+        self._ws = workspace
+        self._ws_key = None if workspace is None else "caller"
+
+    def _workspace(self, q: torch.Tensor) -> torch.Tensor:
+        if self._ws_key == "caller":
+            return self._ws
+        H, N, _ = q.shape
+        key = (H, N, q.device)
+        if self._ws_key != key:
+            self._ws = torch.empty(max(calibatt_sparse_attn_fwd_workspace(H, N), 16),
+                                   dtype=torch.uint8, device=q.device)
+            self._ws_key = key
+        return self._ws
 
     def forward(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, t: int, l: int) -> torch.Tensor:
         e = self.bank.lookup(t, l)
@@ -203,4 +228,4 @@ class CalibAttention(torch.nn.Module):
                 flags = self._flags[e.entry] = torch.from_numpy(e.repeat_flags.copy())
         grid = list(e.grid) if (e.any_repeat and e.grid is not None) else None
         return torch.ops.calibatt.sparse_attn(q, k, v, e.kv_offsets, e.kv_indices, flags, grid,
-                                              float(self.scale))
+                                              float(self.scale), self._workspace(q))

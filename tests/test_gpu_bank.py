@@ -61,6 +61,17 @@ def test_bank_attention_matches_direct_call_and_oracle(gpu, tmp_path):
                     want = oracle.block_sparse_attention(qb[h], kb[h], vb[h], scale, mask[h])
                 e_ = assert_attn_close(f64(o_bank[h]), want, f"(t, l) = ({t}, {l}) head {h}")
             say(f"  (t, l) = ({t}, {l}) entry {e}: last head max-abs {e_[0]:.2e}")
+    # one V^T workspace serves every call of the module
+    ws = attn._workspace(q)
+    assert ws.numel() == gpu.calibatt_sparse_attn_fwd_workspace(H, N)
+    ptr = ws.data_ptr()
+    o1 = attn(q, k, v, 1, 0)
+    assert attn._workspace(q).data_ptr() == ptr
+    # a caller-owned workspace gives the same output
+    own = torch.empty(gpu.calibatt_sparse_attn_fwd_workspace(H, N), dtype=torch.uint8, device=DEV)
+    o2 = CalibAttention(bank, scale, workspace=own)(q, k, v, 1, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
     bank.close()
 
 
