@@ -230,6 +230,44 @@ def test_full_size_layer_sampled(gpu, name, part, parts):
             say(f"  {name} head {h}: max-abs {e[0]:.2e} rel-fro {e[1]:.2e}")
 
 
+MOCHI_REPEAT_CASES = [(flag, part) for flag in (1, 2) for part in range(2)]
+
+
+@pytest.mark.parametrize("flag,part", MOCHI_REPEAT_CASES)
+def test_mochi_repeat_heads_full_output(gpu, flag, part):
+    """Every output token (all 44,520) of the Mochi 480p layer's repeat heads
+    (three of the six per case), plain (flag 1) or keeping the head's block
+    mask (flag 2), against the oracle; and every spatial row equals its
+    anchor row bit for bit at this shape."""
+    w = ATTN_WORKLOADS["mochi1_480p_layer"]
+    say(f"case Mochi repeat heads full output flag={flag} part {part}/2")
+    q, k, v = qkv(w, device=DEV)
+    mask = block_mask(w)
+    flags = repeat_flags(w) * flag
+    F, Hs, W, kk = w.grid.frames, w.grid.rows, w.grid.cols, w.anchors
+    o, _, _ = run(gpu, q, k, v, mask, w.scale, flags, (F, Hs, W, kk))
+    arow = oracle.anchor_of_row(Hs, kk)
+    heads = np.flatnonzero(flags)[part::2]
+    assert heads.size == 3
+    for h in heads:
+        og = o[h].view(F, Hs, W, 128)
+        for y in range(Hs):
+            assert torch.equal(og[:, y], og[:, int(arow[y])]), (h, y)
+        qb, kb, vb = (oracle.as_f64(bf16_bits(t[h])) for t in (q, k, v))
+        got = f64(o[h])
+        want = np.empty_like(got)
+        step = 4 * Hs * W                                      # four frames per oracle call
+        for t0 in range(0, w.n_tokens, step):
+            toks = np.arange(t0, min(t0 + step, w.n_tokens))
+            if flag == 1:
+                want[toks] = oracle.repeat_head_attention(qb, kb, vb, w.scale, F, Hs, W, kk, toks)
+            else:
+                want[toks] = oracle.repeat_head_attention_masked(qb, kb, vb, w.scale, F, Hs, W, kk,
+                                                                 mask[h], toks)
+        e = assert_attn_close(got, want, f"repeat head {h} flag {flag}")
+        say(f"  head {h}: max-abs {e[0]:.2e} rel-fro {e[1]:.2e} over {w.n_tokens} tokens")
+
+
 def test_mfma_rate_probe(gpu):
     """The matrix-core probe runs through the C ABI and reports a rate
     between a tenth of the published dense bf16 peak and that peak."""
@@ -428,6 +466,41 @@ def test_graph_capture_replays_match_eager(gpu, kind):
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(o, want), f"replay {rep}"
+
+
+def test_side_stream_scratch_is_not_reused_early(gpu):
+    """Calls on an explicit side stream with library scratch allocated by the
+    binding (V^T workspace, energy workspace): right after each call returns,
+    the current stream allocates and overwrites a large buffer while the side
+    stream may still be running. The scratch is allocated on the side
+    stream, so the allocator cannot hand it out before that work is done;
+    the results equal the same calls made on the current stream."""
+    say("case side-stream scratch")
+    H, N = 8, 9000
+    q, k, v = (gaussian_bf16(520 + i, (H, N, 128)).to(DEV) for i in range(3))
+    mask = bernoulli_mask(523, H, n_blocks(N), 0.6, True)
+    off, idx = gpu.compile_skiplist(torch.from_numpy(mask).to(DEV))
+    want = gpu.sparse_attention(q, k, v, off, idx, 0.1)
+    want_e = gpu.block_energy(q[:2], k[:2], 0.1)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    for rep in range(3):
+        o = torch.empty_like(q)
+        o.record_stream(side)
+        e = torch.empty_like(want_e)
+        e.record_stream(side)
+        gpu.calibatt_sparse_attn_fwd(q, k, v, o, off, idx, 0.1, stream=side)
+        junk = torch.full((gpu.calibatt_sparse_attn_fwd_workspace(H, N) // 2,), 7.0,
+                          dtype=torch.bfloat16, device=DEV)
+        gpu.calibatt_block_energy(q[:2], k[:2], e, 0.1, stream=side)
+        junk2 = torch.full((gpu.calibatt_block_energy_workspace(2, N) // 4,), -1.0,
+                           dtype=torch.float32, device=DEV)
+        side.synchronize()
+        torch.cuda.synchronize()
+        assert torch.equal(o, want), rep
+        assert torch.equal(e, want_e), rep
+        del junk, junk2
 
 
 @pytest.mark.parametrize("N,H", [(1000, 2), (75600, 1)])

@@ -69,6 +69,49 @@ def test_energy_calibration_size_sampled(gpu, part):
         assert_energy_close(f64(e[h])[rows], want, f"energy head {h}")
 
 
+def test_calibration_chain_on_gpu_energies_480p(gpu):
+    """The calibration shape (40 heads, N = 32760, R = 256), four prompt
+    draws: the library's own fp32 energies of all 40 heads go through
+    calibatt_build_mask at eps(0), eps(25) and eps(49); votes and selected
+    counts equal the oracle's greedy selection on those same energies bit
+    for bit, and calibatt_finalize_mask at rho = 1/2 gives exactly
+    oracle.binarize's masks and oracle.compile_skiplist's lists."""
+    w = CALIB_WORKLOADS["calibration_480p"]
+    R = n_blocks(w.n_tokens)
+    draws = 4
+    say(f"case calibration chain H={w.heads} N={w.n_tokens} draws={draws}")
+    basis = calib_basis(w, DEV)
+    E = torch.empty(draws, w.heads, R, R, dtype=torch.float32, device=DEV)
+    for p in range(draws):
+        q, k = calib_draw(w, p, basis, DEV)
+        gpu.calibatt_block_energy(q, k, E[p], w.scale)
+    torch.cuda.synchronize()
+    E_host = E.cpu().numpy()
+    assert np.allclose(E_host.sum(axis=-1), 1.0, atol=1e-5)
+    for t in w.steps:
+        efx = gpu.calibatt_eps_fx(t, w.total_steps, w.eps_floor, w.eps_start, w.eps_rate)
+        assert efx == oracle.eps_fx(oracle.eps_schedule(t, w.total_steps, w.eps_floor,
+                                                        w.eps_start, w.eps_rate))
+        votes = torch.zeros(w.heads, R, R, dtype=torch.uint8, device=DEV)
+        nsel = torch.zeros(draws, w.heads, R, dtype=torch.int32, device=DEV)
+        gpu.calibatt_build_mask(E, efx, votes, nsel)
+        sel_o, nstar_o = oracle.greedy_select(E_host, efx)
+        votes_o = oracle.accumulate_votes(sel_o)
+        assert np.array_equal(nsel.cpu().numpy(), nstar_o), f"n* differ at t={t}"
+        assert np.array_equal(votes.cpu().numpy(), votes_o), f"votes differ at t={t}"
+        mask = torch.empty_like(votes)
+        off = torch.empty(w.heads * R + 1, dtype=torch.int32, device=DEV)
+        idx = torch.empty(w.heads * R * R, dtype=torch.int32, device=DEV)
+        nnz = gpu.calibatt_finalize_mask(votes, draws, *w.rho, mask, off, idx)
+        want_mask = oracle.binarize(votes_o, draws, *w.rho)
+        want_off, want_idx = oracle.compile_skiplist(want_mask)
+        assert np.array_equal(mask.cpu().numpy(), want_mask), f"mask differs at t={t}"
+        assert nnz == want_idx.size
+        assert np.array_equal(off.cpu().numpy(), want_off)
+        assert np.array_equal(idx.cpu().numpy()[:nnz], want_idx)
+        say(f"  t={t}: eps {efx / 2 ** 40:.6f}, mean n* {nstar_o.mean():.1f}, kept {nnz / (w.heads * R * R):.4f}")
+
+
 @pytest.mark.parametrize("kind", ["dirichlet", "peaky", "ties", "uniform", "onehot"])
 @pytest.mark.parametrize("R", [8, 64, 100, 591, 2047])
 def test_select_bit_exact(gpu, kind, R):
