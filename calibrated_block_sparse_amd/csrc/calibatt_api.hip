@@ -34,11 +34,12 @@ int api_ok() {
 }
 
 // Anchor A(m) = floor((2m+1) rows / (2k)) serves the rows y with
-// floor(y k / rows) = m. A(m) k / rows >= m + 1/2 - (2k-1)/(2 rows), so A(m)
-// lies in its own segment whenever rows >= 2k - 1 (and trivially when
-// k == rows); for rows/2 < k < rows some anchor rows would receive another
-// anchor's output instead of their own, which the repeat head's broadcast
-// of each anchor to the rest of its frame does not allow.
+// floor(y k / rows) = m. A repeat head hands each anchor's output to the
+// other rows of its frame, so every anchor row must lie in the segment it
+// serves: floor(A(m) k / rows) == m for every m. This always holds when
+// k == rows or rows >= 2k - 1 (then A(m) k / rows >= m + 1/2 - (2k-1)/(2 rows));
+// for rows/2 < k < rows it holds for some geometries and fails for others
+// (rows = 10, k = 9: row 1 would take row 0's output).
 int check_grid(const char* fn, const calibatt_grid& g, int32_t n_tokens) {
   if (g.frames <= 0 || g.rows <= 0 || g.cols <= 0 ||
       (int64_t)g.frames * g.rows * g.cols != n_tokens)
@@ -47,10 +48,13 @@ int check_grid(const char* fn, const calibatt_grid& g, int32_t n_tokens) {
   if (g.anchors < 1 || g.anchors > g.rows)
     return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: anchors %d not in [1, rows=%d]", fn, g.anchors,
                     g.rows);
-  if (g.anchors != g.rows && g.rows < 2 * g.anchors - 1)
-    return api_fail(CALIBATT_ERR_UNSUPPORTED,
-                    "%s: %d anchors in %d rows: needs anchors == rows or rows >= 2*anchors - 1", fn,
-                    g.anchors, g.rows);
+  for (int64_t m = 0; m < g.anchors; ++m) {
+    const int64_t a = (2 * m + 1) * g.rows / (2 * (int64_t)g.anchors);
+    if (a * g.anchors / g.rows != m)
+      return api_fail(CALIBATT_ERR_UNSUPPORTED,
+                      "%s: %d anchors in %d rows: anchor row %lld would not serve its own segment %lld",
+                      fn, g.anchors, g.rows, (long long)a, (long long)m);
+  }
   return CALIBATT_OK;
 }
 

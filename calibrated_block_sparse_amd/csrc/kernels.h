@@ -76,7 +76,7 @@ int api_ok();
 
 // Checks a video grid for repeat heads and the similarity score: it covers
 // n_tokens, 1 <= anchors <= rows, and every anchor row lies in the segment
-// it serves (anchors == rows or rows >= 2 * anchors - 1).
+// it serves.
 int check_grid(const char* fn, const calibatt_grid& g, int32_t n_tokens);
 
 hipError_t launch_v_transpose(const VtArgs& a, hipStream_t stream);

@@ -113,10 +113,11 @@ int32_t calibatt_abi_version(void);
  *                CALIBATT_ERR_INVALID_ARG
  *   grid         host pointer, required iff a repeat flag is set:
  *                frames*rows*cols == N and 1 <= anchors <= rows
- *                (CALIBATT_ERR_INVALID_ARG otherwise); anchors == rows or
- *                rows >= 2*anchors - 1, so that every anchor row lies in
- *                the segment it serves and keeps its own output
- *                (CALIBATT_ERR_UNSUPPORTED otherwise)
+ *                (CALIBATT_ERR_INVALID_ARG otherwise); every anchor row
+ *                must lie in the segment it serves, floor(A(m)*anchors/rows)
+ *                == m, so that it keeps its own output (always true when
+ *                anchors == rows or rows >= 2*anchors - 1;
+ *                CALIBATT_ERR_UNSUPPORTED otherwise)
  *   workspace    device, 16-byte aligned, at least
  *                calibatt_sparse_attn_fwd_workspace(heads, N) bytes; the call
  *                first writes V there as [heads][R][128 d][128 keys] tiles
@@ -212,7 +213,7 @@ int calibatt_block_energy(const void* q, const void* k, float* energy,
  *
  *   energy_workspace  device, as filled by calibatt_block_energy
  *   grid              frames*rows*cols == N, 1 <= anchors <= rows, cols <= 8192,
- *                     anchors == rows or rows >= 2*anchors - 1 (as for
+ *                     every anchor row in the segment it serves (as for
  *                     calibatt_sparse_attn_fwd)
  *   row_profiles      device fp32 [heads][frames*rows][R], output
  *   similarity        device fp32 [heads], output

@@ -97,14 +97,17 @@ def block_sparse_attention(q, k, v, scale: float, mask) -> np.ndarray:
 def check_anchor_geometry(rows: int, anchors: int) -> None:
     """The repeat head computes its anchor rows and hands each one's output
     to the other rows of its frame ([CalibAtt blog] §三), so every anchor
-    row must keep its own output: A(m) must lie in the segment m it serves.
-    That holds when anchors == rows or rows >= 2 * anchors - 1; other
-    geometries (rows / 2 < anchors < rows) are rejected."""
+    row must keep its own output: A(m) must lie in the segment m it serves,
+    floor(A(m) * anchors / rows) == m. Geometries where some anchor does not
+    (possible only for rows / 2 < anchors < rows, e.g. 9 anchors in 10 rows)
+    are rejected."""
     if not 1 <= anchors <= rows:
         raise ValueError(f"anchors {anchors} not in [1, rows={rows}]")
-    if anchors != rows and rows < 2 * anchors - 1:
-        raise ValueError(f"{anchors} anchors in {rows} rows: some anchor rows would not serve "
-                         "their own segment")
+    for m in range(anchors):
+        a = (2 * m + 1) * rows // (2 * anchors)
+        if a * anchors // rows != m:
+            raise ValueError(f"{anchors} anchors in {rows} rows: anchor row {a} would not serve "
+                             f"its own segment {m}")
 
 
 def anchor_rows(rows: int, anchors: int) -> np.ndarray:

@@ -93,9 +93,10 @@ def test_attention_argument_errors(lib):
     assert attn(lib, flags=flags, grid=ctypes.byref(g)) == -1
     g = cbs.Grid(2, 16, 32, 17)                                # anchors > rows
     assert attn(lib, flags=flags, grid=ctypes.byref(g)) == -1
-    g = cbs.Grid(2, 16, 32, 9)                                 # 16 < 2*9 - 1: anchors off their segments
-    assert attn(lib, flags=flags, grid=ctypes.byref(g)) == -2
-    assert "anchors" in cbs.calibatt_last_error()
+    g = cbs.Grid(2, 10, 50, 9)                                 # anchor row 1 would serve segment 0
+    assert attn(lib, flags=flags, grid=ctypes.byref(g), n=1000, sh=1000 * 128,
+                wsb=cbs.calibatt_sparse_attn_fwd_workspace(2, 1000)) == -2
+    assert "anchor" in cbs.calibatt_last_error()
     g = cbs.Grid(2, 16, 32, 5)
     assert attn(lib, flags=(ctypes.c_uint8 * 2)(0, 3), grid=ctypes.byref(g)) == -1   # flag 3
     g = cbs.Grid(2, 450, 128, 5)                               # N = 115200: R = 900 > 896

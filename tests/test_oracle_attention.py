@@ -135,11 +135,13 @@ def test_anchor_rows_closed_form():
 
 
 def test_every_anchor_serves_itself_where_supported():
-    """Brute force over small geometries: where the oracle accepts (anchors
-    == rows or rows >= 2 anchors - 1), every anchor row is served by itself
-    and the served rows of each anchor are contiguous; everywhere else the
-    rule would hand some anchor row another anchor's output, and the oracle
-    rejects the geometry."""
+    """Brute force over small geometries: the oracle accepts exactly the
+    (rows, anchors) where every anchor row is served by itself (checked
+    here by building the row -> anchor map and looking at each anchor),
+    which includes every geometry with anchors == rows or rows >=
+    2 anchors - 1; the rejected ones are those where some anchor row would
+    take another anchor's output."""
+    rejected = 0
     for Hs in range(1, 41):
         for k in range(1, Hs + 1):
             m = np.arange(k)
@@ -148,13 +150,18 @@ def test_every_anchor_serves_itself_where_supported():
             self_served = all(a[y] == y for y in A)
             if k == Hs or Hs >= 2 * k - 1:
                 assert self_served, (Hs, k)
+            if self_served:
                 assert list(oracle.anchor_of_row(Hs, k)) == list(a)
             else:
+                rejected += 1
                 with pytest.raises(ValueError):
                     oracle.anchor_rows(Hs, k)
-    # the example of a rejected geometry: 10 rows, 9 anchors (row 1 would copy row 0)
+    assert rejected > 0
+    # the example of a rejected geometry: 10 rows, 9 anchors (row 1 would copy row 0);
+    # 8 rows with 5 anchors is accepted (anchors 0, 2, 4, 5, 7 each serve themselves)
     with pytest.raises(ValueError):
         oracle.anchor_of_row(10, 9)
+    assert list(oracle.anchor_rows(8, 5)) == [0, 2, 4, 5, 7]
 
 
 def test_repeat_head_reduces_to_dense_when_every_row_is_an_anchor():
