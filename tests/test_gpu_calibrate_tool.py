@@ -66,7 +66,7 @@ def test_driver_votes_monotone_density_and_bank(gpu, tmp_path):
         _, off, idx, flags = bank.lookup_host(i, 0)
         assert np.array_equal(off, fin[t][1].cpu().numpy())
         assert np.array_equal(idx, fin[t][2].cpu().numpy())
-    say(f"  density at rho 0.5: {[rep[str(t)]['density']['0.5'] for t in (0, 25, 49)]}")
+    say(f"  density at rho 0.5: {[rep[t]['density']['0.5'] for t in (0, 25, 49)]}")
 
 
 def test_driver_few_step_schedule_and_cli(gpu, capsys):
