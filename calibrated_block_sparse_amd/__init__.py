@@ -20,6 +20,7 @@ import torch
 BLOCK = 128
 HEAD_DIM = 128
 MAX_BLOCKS = 2047
+NOALLOC_SCRATCH_BYTES = 268435456   # CALIBATT_NOALLOC_SCRATCH_BYTES
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libcalibatt.so")
@@ -39,6 +40,9 @@ SIGNATURES = {
     "calibatt_sparse_attn_fwd_vt": (_c.c_int, [_p, _p, _p, _p, _c.c_int32, _c.c_int32,
                                                _c.c_int32, _c.c_int64, _c.c_int64, _c.c_float,
                                                _p, _p, _c.c_int64, _p, _p, _c.c_size_t, _p]),
+    "calibatt_sparse_attn_fwd_noalloc": (_c.c_int, [_p, _p, _p, _p, _c.c_int32, _c.c_int32,
+                                                    _c.c_int32, _c.c_int64, _c.c_int64, _c.c_float,
+                                                    _p, _p, _c.c_int64, _p, _p, _p]),
     "calibatt_block_energy_workspace": (_c.c_size_t, [_c.c_int32, _c.c_int32]),
     "calibatt_block_energy": (_c.c_int, [_p, _p, _p, _c.c_int32, _c.c_int32, _c.c_int32,
                                          _c.c_int64, _c.c_int64, _c.c_float, _p, _c.c_size_t, _p]),
@@ -259,6 +263,21 @@ def calibatt_sparse_attn_fwd_vt(q, k, vt, o, kv_offsets, kv_indices, scale: floa
         None if g is None else ctypes.byref(g), vt.numel() * vt.element_size(),
         _stream(stream, q, k, vt, o, kv_offsets, kv_indices))
     _check("calibatt_sparse_attn_fwd_vt", rc)
+
+
+def calibatt_sparse_attn_fwd_noalloc(q, k, v, o, kv_offsets, kv_indices, scale: float,
+                                     repeat_flags=None, grid=None, stream=None) -> None:
+    """As calibatt_sparse_attn_fwd, with the V^T tiles in the library's own
+    device scratch instead of a workspace (nothing is allocated; calls that
+    overlap on one device race)."""
+    H, N, D, sh, stok = _attn_layout("calibatt_sparse_attn_fwd_noalloc", q, k, v, o)
+    nnz = _check_lists(H, N, kv_offsets, kv_indices)
+    flags, g = _flags_grid(H, repeat_flags, grid)
+    rc = load_library().calibatt_sparse_attn_fwd_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), H, N, D, sh, stok, float(scale), _ptr(kv_offsets),
+        _ptr(kv_indices), nnz, None if flags is None else flags.ctypes.data_as(ctypes.c_void_p),
+        None if g is None else ctypes.byref(g), _stream(stream, q, k, v, o, kv_offsets, kv_indices))
+    _check("calibatt_sparse_attn_fwd_noalloc", rc)
 
 
 def calibatt_block_energy_workspace(heads: int, n_tokens: int) -> int:

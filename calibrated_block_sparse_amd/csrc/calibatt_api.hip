@@ -6,7 +6,9 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
+#include <unordered_map>
 #include <vector>
 
 #include "../../include/calibatt.h"
@@ -97,7 +99,7 @@ extern "C" {
 
 const char* calibatt_last_error(void) { return calibatt::g_last_error.c_str(); }
 
-int32_t calibatt_abi_version(void) { return 7; }
+int32_t calibatt_abi_version(void) { return 8; }
 
 
 size_t calibatt_sparse_attn_fwd_workspace(int32_t heads, int32_t n_tokens) {
@@ -233,23 +235,14 @@ int calibatt_sparse_attn_fwd_vt(const void* q, const void* k, const void* vt, vo
                    kv_indices, nnz, repeat_flags, grid, static_cast<hipStream_t>(stream));
 }
 
-int calibatt_sparse_attn_fwd(const void* q, const void* k, const void* v, void* o, int32_t heads,
-                             int32_t n_tokens, int32_t head_dim, int64_t stride_head,
-                             int64_t stride_token, float scale, const int32_t* kv_offsets,
-                             const int32_t* kv_indices, int64_t nnz,
-                             const uint8_t* repeat_flags, const calibatt_grid* grid,
-                             void* workspace, size_t workspace_bytes, void* stream) {
-  const char* fn = "calibatt_sparse_attn_fwd";
-  int rc = check_tensor_layout(fn, heads, n_tokens, head_dim, stride_head, stride_token);
-  if (rc) return rc;
-  if (heads == 0 || n_tokens == 0) return api_ok();
-  rc = check_workspace(fn, heads, n_tokens, workspace, workspace_bytes);
-  if (rc) return rc;
-  if (!v) return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: null q/k/v/o", fn);
-  if (!aligned16(v)) return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: q/k/v/o must be 16-byte aligned", fn);
-  // validate everything the attention needs before enqueuing the pre-pass
-  if (!q || !k || !o) return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: null q/k/v/o", fn);
-  if (!aligned16(q) || !aligned16(k) || !aligned16(o))
+// Everything the full attention call needs from its arguments besides the
+// tensor layout and the workspace, checked before anything is enqueued.
+static int check_attn_inputs(const char* fn, const void* q, const void* k, const void* v,
+                             const void* o, int32_t heads, int32_t n_tokens, float scale,
+                             const int32_t* kv_offsets, const int32_t* kv_indices, int64_t nnz,
+                             const uint8_t* repeat_flags, const calibatt_grid* grid) {
+  if (!q || !k || !v || !o) return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: null q/k/v/o", fn);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
     return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: q/k/v/o must be 16-byte aligned", fn);
   if (!(scale > 0.f) || !std::isfinite(scale))
     return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: scale must be finite and > 0", fn);
@@ -272,6 +265,27 @@ int calibatt_sparse_attn_fwd(const void* q, const void* k, const void* v, void* 
   }
   if (any_sparse && (!kv_offsets || (!kv_indices && nnz > 0)))
     return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: null kept-block list", fn);
+  if ((int64_t)heads * ceil_div(n_tokens, CALIBATT_BLOCK) > 0x7fffffff)
+    return api_fail(CALIBATT_ERR_UNSUPPORTED, "%s: too many tiles", fn);
+  return CALIBATT_OK;
+}
+
+int calibatt_sparse_attn_fwd(const void* q, const void* k, const void* v, void* o, int32_t heads,
+                             int32_t n_tokens, int32_t head_dim, int64_t stride_head,
+                             int64_t stride_token, float scale, const int32_t* kv_offsets,
+                             const int32_t* kv_indices, int64_t nnz,
+                             const uint8_t* repeat_flags, const calibatt_grid* grid,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "calibatt_sparse_attn_fwd";
+  int rc = check_tensor_layout(fn, heads, n_tokens, head_dim, stride_head, stride_token);
+  if (rc) return rc;
+  if (heads == 0 || n_tokens == 0) return api_ok();
+  rc = check_workspace(fn, heads, n_tokens, workspace, workspace_bytes);
+  if (rc) return rc;
+  // validate everything the attention needs before enqueuing the pre-pass
+  rc = check_attn_inputs(fn, q, k, v, o, heads, n_tokens, scale, kv_offsets, kv_indices, nnz,
+                         repeat_flags, grid);
+  if (rc) return rc;
   rc = calibatt_prepare_vt(v, heads, n_tokens, head_dim, stride_head, stride_token, workspace,
                            workspace_bytes, stream);
   if (rc) return rc;
@@ -495,3 +509,98 @@ int calibatt_mfma_rate_probe(float* sink, int64_t iters, int32_t workgroups, voi
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Attention without allocation or workspace (calibatt_sparse_attn_fwd_noalloc).
+//
+// The V^T tiles go to `scratch`, a file-scope device array of
+// CALIBATT_NOALLOC_SCRATCH_BYTES that every device the library runs on holds
+// for the life of the process. In host code `scratch` names a host-side
+// stand-in, not device memory: its device address is looked up once per
+// device with hipGetSymbolAddress (with that device current) and only that
+// address is ever handed to a kernel.
+
+static __device__ __align__(256) uint8_t scratch[CALIBATT_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex g_scratch_mu;
+std::unordered_map<int, void*> g_scratch_addr;  // device -> its copy of `scratch`
+
+// Device address of `scratch` on the device `stream` belongs to.
+int scratch_address(const char* fn, hipStream_t stream, void** out) {
+  int dev = -1;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  const auto it = g_scratch_addr.find(dev);
+  if (it != g_scratch_addr.end()) {
+    *out = it->second;
+    return CALIBATT_OK;
+  }
+  int cur = -1;
+  if ((e = hipGetDevice(&cur)) != hipSuccess) return hip_fail(e, fn);
+  if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return hip_fail(e, fn);
+  void* p = nullptr;
+  e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  const hipError_t back = cur != dev ? hipSetDevice(cur) : hipSuccess;
+  if (e != hipSuccess) return hip_fail(e, fn);
+  if (back != hipSuccess) return hip_fail(back, fn);
+  if (!p) return api_fail(CALIBATT_ERR_HIP, "%s: no device address for the scratch array", fn);
+  g_scratch_addr.emplace(dev, p);
+  *out = p;
+  return CALIBATT_OK;
+}
+
+}  // namespace
+
+extern "C" int calibatt_sparse_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o,
+                                                int32_t heads, int32_t n_tokens, int32_t head_dim,
+                                                int64_t stride_head, int64_t stride_token, float scale,
+                                                const int32_t* kv_offsets, const int32_t* kv_indices,
+                                                int64_t nnz, const uint8_t* repeat_flags,
+                                                const calibatt_grid* grid, void* stream) {
+  const char* fn = "calibatt_sparse_attn_fwd_noalloc";
+  int rc = check_tensor_layout(fn, heads, n_tokens, head_dim, stride_head, stride_token);
+  if (rc) return rc;
+  if (heads == 0 || n_tokens == 0) return api_ok();
+  const int64_t R = ceil_div(n_tokens, CALIBATT_BLOCK);
+  constexpr int64_t kTile = (int64_t)CALIBATT_BLOCK * CALIBATT_HEAD_DIM * 2;
+  constexpr int64_t kMaxTiles = (int64_t)CALIBATT_NOALLOC_SCRATCH_BYTES / kTile;
+  if (R > kMaxTiles)
+    return api_fail(CALIBATT_ERR_UNSUPPORTED,
+                    "%s: N = %d needs %lld V^T tiles per head; the %d-byte scratch holds %lld "
+                    "(N <= %lld)", fn, n_tokens, (long long)R, CALIBATT_NOALLOC_SCRATCH_BYTES,
+                    (long long)kMaxTiles, (long long)(kMaxTiles * CALIBATT_BLOCK));
+  rc = check_attn_inputs(fn, q, k, v, o, heads, n_tokens, scale, kv_offsets, kv_indices, nnz,
+                         repeat_flags, grid);
+  if (rc) return rc;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  void* vt = nullptr;
+  if ((rc = scratch_address(fn, st, &vt))) return rc;
+  // heads in equal chunks whose V^T tiles fit the scratch; each chunk's
+  // pre-pass and attention run back to back on the stream
+  const int64_t fit = kMaxTiles / R;
+  const int64_t chunks = ceil_div(heads, fit);
+  const int32_t per = (int32_t)ceil_div(heads, chunks);
+  for (int32_t h0 = 0; h0 < heads; h0 += per) {
+    const int32_t hc = heads - h0 < per ? heads - h0 : per;
+    const int64_t off = (int64_t)h0 * stride_head;
+    VtArgs t;
+    t.v = static_cast<const uint16_t*>(v) + off;
+    t.vt = static_cast<uint16_t*>(vt);
+    t.stride_head = stride_head;
+    t.stride_token = stride_token;
+    t.heads = hc;
+    t.n_tokens = n_tokens;
+    t.n_blocks = (int32_t)R;
+    const hipError_t e = launch_v_transpose(t, st);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    rc = attn_core(fn, static_cast<const uint16_t*>(q) + off, static_cast<const uint16_t*>(k) + off,
+                   vt, static_cast<uint16_t*>(o) + off, hc, n_tokens, stride_head, stride_token,
+                   scale, kv_offsets ? kv_offsets + (int64_t)h0 * R : nullptr, kv_indices, nnz,
+                   repeat_flags ? repeat_flags + h0 : nullptr, grid, st);
+    if (rc) return rc;
+  }
+  return api_ok();
+}

@@ -54,6 +54,7 @@ enum {
 #define CALIBATT_HEAD_DIM 128
 #define CALIBATT_MAX_BLOCKS 2047 /* R limit of the selection kernels */
 #define CALIBATT_MAX_STRIDE_TOKEN 8388608 /* elements between tokens (2^23) */
+#define CALIBATT_NOALLOC_SCRATCH_BYTES 268435456 /* device scratch of _noalloc (256 MiB per device) */
 
 /* Latent video grid of a sequence: token n = f*rows*cols + y*cols + x
  * (frame-major, row-major inside a frame; [CalibAtt blog] §六). `anchors`
@@ -73,7 +74,8 @@ const char* calibatt_last_error(void);
  * calibatt_prepare_vt and calibatt_sparse_attn_fwd_vt, version 4 the
  * single-pass energy workspace and calibatt_mfma_rate_probe, version 5 the
  * mask bank (calibatt_bank_*) and CALIBATT_ERR_IO, version 6
- * calibatt_spatial_similarity, version 7 masked repeat heads (flag 2). */
+ * calibatt_spatial_similarity, version 7 masked repeat heads (flag 2),
+ * version 8 calibatt_sparse_attn_fwd_noalloc. */
 int32_t calibatt_abi_version(void);
 
 /*
@@ -169,6 +171,31 @@ int calibatt_sparse_attn_fwd_vt(const void* q, const void* k, const void* vt, vo
                                 const int32_t* kv_offsets, const int32_t* kv_indices,
                                 int64_t nnz, const uint8_t* repeat_flags,
                                 const calibatt_grid* grid, size_t vt_bytes, void* stream);
+
+/*
+ * For callers that cannot allocate device memory or pass a workspace: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation. Same arguments and results as calibatt_sparse_attn_fwd (bit
+ * for bit) without workspace / workspace_bytes. The V^T tiles go to a
+ * device array inside the library of CALIBATT_NOALLOC_SCRATCH_BYTES, which
+ * each device the library runs on holds until the process ends (its address
+ * is looked up on the first call on a device; no allocation is made by this
+ * call). Heads are processed in equal chunks whose tiles fit it (at most
+ * floor(8192 / R) heads per chunk: one V^T pre-pass and one attention
+ * launch per chunk), so N may not exceed 8192 * 128 = 1,048,576 tokens
+ * (CALIBATT_ERR_UNSUPPORTED beyond). Every call on a device shares that
+ * device's array: calls that overlap on one device (on different streams,
+ * or from several threads) race and give wrong results; nothing in the
+ * array needs to start at any value. Capturable in a HIP graph like the
+ * full call (kernel launches only) once a first call on the device has
+ * looked up the array's address.
+ */
+int calibatt_sparse_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o,
+                                     int32_t heads, int32_t n_tokens, int32_t head_dim,
+                                     int64_t stride_head, int64_t stride_token, float scale,
+                                     const int32_t* kv_offsets, const int32_t* kv_indices,
+                                     int64_t nnz, const uint8_t* repeat_flags,
+                                     const calibatt_grid* grid, void* stream);
 
 /*
  * Bytes of device workspace calibatt_block_energy needs: 8 * heads * R*128 *

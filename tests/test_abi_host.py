@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version(lib):
-    assert cbs.calibatt_abi_version() == 7
+    assert cbs.calibatt_abi_version() == 8
 
 
 def fake(n=16):
@@ -105,6 +105,20 @@ def test_attention_argument_errors(lib):
     assert big(flags=(ctypes.c_uint8 * 2)(0, 2), grid=ctypes.byref(g)) == -2
     # empty problems are no-ops and succeed
     assert attn(lib, heads=0) == 0 and attn(lib, n=0) == 0
+
+
+def test_noalloc_argument_errors(lib):
+    """calibatt_sparse_attn_fwd_noalloc checks its arguments as the full call
+    does and rejects N beyond what its fixed scratch holds (8192 V^T tiles
+    per head: N <= 1,048,576) before touching a device."""
+    na = lambda **kw: lib.calibatt_sparse_attn_fwd_noalloc(
+        kw.get("q", fake()), fake(), fake(), fake(), kw.get("heads", 2), kw.get("n", 1024), 128,
+        kw.get("n", 1024) * 128, 128, kw.get("scale", 0.088), fake(), fake(), 10, None, None, None)
+    assert na(n=8192 * 128 + 1) == -2
+    assert "scratch" in cbs.calibatt_last_error()
+    assert na(q=None) == -1
+    assert na(scale=-1.0) == -1
+    assert na(heads=0) == 0 and na(n=0) == 0
 
 
 def test_energy_argument_errors(lib):
