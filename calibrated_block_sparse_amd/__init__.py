@@ -284,10 +284,15 @@ def calibatt_block_energy_workspace(heads: int, n_tokens: int) -> int:
     return int(load_library().calibatt_block_energy_workspace(heads, n_tokens))
 
 
+ENERGY_WORKSPACE_CAP = 2 << 30   # bytes the binding allocates at most (heads then go in chunks)
+
+
 def calibatt_block_energy(q, k, energy, scale: float, workspace=None, stream=None) -> None:
     """energy (fp32 CUDA [H][R][R]) <- block energies of softmax(scale q k^T).
-    workspace: uint8 CUDA tensor of calibatt_block_energy_workspace bytes
-    (allocated here through torch when None)."""
+    workspace: uint8 CUDA tensor of at least calibatt_block_energy_workspace(1,
+    N) bytes (heads are processed in chunks of as many as it holds); when
+    None, one of min(all heads, max(one head, 2 GiB)) is allocated here
+    through torch."""
     H, N, D, sh, stok = _attn_layout("calibatt_block_energy", q, k)
     R = n_blocks(N)
     if energy.dtype != torch.float32 or not energy.is_contiguous() or energy.shape != (H, R, R):
@@ -295,7 +300,8 @@ def calibatt_block_energy(q, k, energy, scale: float, workspace=None, stream=Non
     need = calibatt_block_energy_workspace(H, N)
     st = _launch_stream(stream, q, k, energy, workspace)
     if workspace is None:
-        workspace = _empty_on(st, max(need, 1), dtype=torch.uint8, device=q.device)
+        size = min(need, max(calibatt_block_energy_workspace(1, N), ENERGY_WORKSPACE_CAP))
+        workspace = _empty_on(st, max(size, 1), dtype=torch.uint8, device=q.device)
     rc = load_library().calibatt_block_energy(_ptr(q), _ptr(k), _ptr(energy), H, N, D, sh, stok,
                                               float(scale), _ptr(workspace),
                                               workspace.numel() * workspace.element_size(),

@@ -318,25 +318,33 @@ int calibatt_block_energy(const void* q, const void* k, float* energy, int32_t h
     return api_fail(CALIBATT_ERR_UNSUPPORTED, "%s: %lld blocks > %d", fn, (long long)R,
                 CALIBATT_MAX_BLOCKS);
   if ((int64_t)heads * R > 0x7fffffff) return api_fail(CALIBATT_ERR_UNSUPPORTED, "%s: too many tiles", fn);
-  const size_t need = calibatt_block_energy_workspace(heads, n_tokens);
-  if (!workspace || workspace_bytes < need)
-    return api_fail(CALIBATT_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu", fn, workspace_bytes, need);
-  if (reinterpret_cast<uintptr_t>(workspace) & 7u)
-    return api_fail(CALIBATT_ERR_WORKSPACE, "%s: workspace must be 8-byte aligned", fn);
-  EnergyArgs a;
-  a.q = static_cast<const uint16_t*>(q);
-  a.k = static_cast<const uint16_t*>(k);
-  a.stride_head = stride_head;
-  a.stride_token = stride_token;
-  a.partials = static_cast<float*>(workspace);
-  a.row_stats = a.partials + (size_t)2 * heads * R * R * CALIBATT_BLOCK;
-  a.energy = energy;
-  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
-  a.n_tokens = n_tokens;
-  a.n_blocks = (int32_t)R;
-  a.heads = heads;
-  hipError_t e = launch_block_energy(a, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, fn);
+  // heads go in chunks of as many as the workspace holds (all at once when
+  // it holds them all; the results do not depend on the chunking)
+  const size_t per_head = calibatt_block_energy_workspace(1, n_tokens);
+  if (!workspace || workspace_bytes < per_head)
+    return api_fail(CALIBATT_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu (one head)", fn,
+                    workspace_bytes, per_head);
+  if (reinterpret_cast<uintptr_t>(workspace) & 15u)
+    return api_fail(CALIBATT_ERR_WORKSPACE, "%s: workspace must be 16-byte aligned", fn);
+  const int32_t chunk = workspace_bytes / per_head >= (size_t)heads ? heads
+                                                                     : (int32_t)(workspace_bytes / per_head);
+  for (int32_t h0 = 0; h0 < heads; h0 += chunk) {
+    const int32_t hc = heads - h0 < chunk ? heads - h0 : chunk;
+    EnergyArgs a;
+    a.q = static_cast<const uint16_t*>(q) + (int64_t)h0 * stride_head;
+    a.k = static_cast<const uint16_t*>(k) + (int64_t)h0 * stride_head;
+    a.stride_head = stride_head;
+    a.stride_token = stride_token;
+    a.partials = static_cast<float*>(workspace);
+    a.row_stats = a.partials + (size_t)2 * hc * R * R * CALIBATT_BLOCK;
+    a.energy = energy + (int64_t)h0 * R * R;
+    a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+    a.n_tokens = n_tokens;
+    a.n_blocks = (int32_t)R;
+    a.heads = hc;
+    hipError_t e = launch_block_energy(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, fn);
+  }
   return api_ok();
 }
 

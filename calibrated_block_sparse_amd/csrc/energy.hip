@@ -15,7 +15,8 @@
 // fix-up's change of reference are exact powers of two.
 //
 // energy_fixup_kernel: E[r][c] = (1/|I_r|) sum_i s_c(i) 2^(m_c(i) - m(i)) / l(i),
-// summed in ascending i, so the result is bitwise reproducible.
+// summed in a fixed order (four consecutive rows per lane, then a butterfly
+// over 32 lanes), so the result is bitwise reproducible.
 //
 // K tiles are copied global -> LDS by the load unit (two buffers: the copy of
 // block c+1 runs under the whole computation of block c); operand reads are
@@ -167,6 +168,11 @@ __global__ void __launch_bounds__(kThreads, 2) energy_partials_kernel(const Ener
   if (g == 0 && qvalid) reinterpret_cast<float2*>(a.row_stats)[(int64_t)head * np + qi] = float2{m_run, ltot};
 }
 
+// One workgroup per (head, block-row r). Half-wave h of wave w takes key
+// blocks c = 2w + h, 2w + h + 8, ...; lane j of the half-wave reads the
+// partials of query rows 4j .. 4j+3 of block c (32 contiguous bytes, so a
+// half-wave reads block c's 128 partials as one 1 KiB run), sums its four
+// rows in order, and the 32 lanes combine by a fixed butterfly.
 __global__ void __launch_bounds__(kThreads) energy_fixup_kernel(const EnergyArgs a) {
   __shared__ float s_m[kBlock], s_inv[kBlock];
   const int R = a.n_blocks, N = a.n_tokens;
@@ -174,24 +180,42 @@ __global__ void __launch_bounds__(kThreads) energy_fixup_kernel(const EnergyArgs
   const int64_t np = (int64_t)R * kBlock;
   const int rows = (r + 1) * kBlock <= N ? kBlock : N - r * kBlock;
   const float2* __restrict__ st = reinterpret_cast<const float2*>(a.row_stats) + (int64_t)head * np + r * kBlock;
-  if ((int)threadIdx.x < rows) {
-    const float2 v = st[threadIdx.x];
+  if ((int)threadIdx.x < kBlock) {
+    // rows past N were never written: reference 0 and factor 0
+    const bool ok = (int)threadIdx.x < rows;
+    const float2 v = ok ? st[threadIdx.x] : float2{0.f, 1.f};
     s_m[threadIdx.x] = v.x;
-    s_inv[threadIdx.x] = 1.f / v.y;
+    s_inv[threadIdx.x] = ok ? 1.f / v.y : 0.f;
   }
   __syncthreads();
   const float inv_rows = 1.f / (float)rows;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int half = lane >> 5, j = lane & 31;
+  const int i0 = 4 * j;
   const float2* __restrict__ part =
-      reinterpret_cast<const float2*>(a.partials) + (int64_t)head * R * np + r * kBlock;
+      reinterpret_cast<const float2*>(a.partials) + (int64_t)head * R * np + r * kBlock + i0;
   float* out = a.energy + ((int64_t)head * R + r) * R;
-  for (int c = threadIdx.x; c < R; c += kThreads) {
-    const float2* p = part + (int64_t)c * np;
+  float f[4], m[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    f[k] = s_inv[i0 + k];
+    m[k] = s_m[i0 + k];
+  }
+  for (int c0 = 2 * wave; c0 < R; c0 += 2 * (kThreads / 64)) {
+    const int c = c0 + half;
     float acc = 0.f;
-    for (int i = 0; i < rows; ++i) {
-      const float2 v = p[i];
-      acc = __builtin_fmaf(v.x, __builtin_ldexpf(s_inv[i], (int)(v.y - s_m[i])), acc);
+    if (c < R) {
+      const float4* p = reinterpret_cast<const float4*>(part + (int64_t)c * np);
+      const float4 v01 = p[0], v23 = p[1];
+      const float s[4] = {v01.x, v01.z, v23.x, v23.z};
+      const float e[4] = {v01.y, v01.w, v23.y, v23.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (i0 + k < rows) acc = __builtin_fmaf(s[k], __builtin_ldexpf(f[k], (int)(e[k] - m[k])), acc);
     }
-    out[c] = acc * inv_rows;
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 32);
+    if (j == 0 && c < R) out[c] = acc * inv_rows;
   }
 }
 

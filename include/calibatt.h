@@ -214,7 +214,14 @@ size_t calibatt_block_energy_workspace(int32_t heads, int32_t n_tokens);
  *
  *   q, k       device bf16 [heads][N][128], strides as above
  *   energy     device fp32 [heads][R][R], output (dense, row-major)
- *   workspace  device, 8-byte aligned, >= calibatt_block_energy_workspace(heads, N) bytes
+ *   workspace  device, 16-byte aligned, at least
+ *              calibatt_block_energy_workspace(1, N) bytes. Heads are
+ *              processed in chunks of as many as it holds
+ *              (workspace_bytes / calibatt_block_energy_workspace(1, N),
+ *              all of them when it holds calibatt_block_energy_workspace(
+ *              heads, N)); the energies do not depend on the chunking. Only
+ *              a workspace that held every head can be passed on to
+ *              calibatt_spatial_similarity.
  */
 int calibatt_block_energy(const void* q, const void* k, float* energy,
                           int32_t heads, int32_t n_tokens, int32_t head_dim,

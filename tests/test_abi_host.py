@@ -129,8 +129,10 @@ def test_energy_argument_errors(lib):
                                                128, 0.1, kw.get("ws", fake()), kw.get("wsb", ws), None)
     assert f(d=96) == -2
     assert f(q=None) == -1
-    assert f(wsb=ws - 1) == -4
+    # a workspace for one head is enough (heads then go in chunks); less is not
+    assert f(wsb=cbs.calibatt_block_energy_workspace(1, 1000) - 1) == -4
     assert f(ws=None) == -4
+    assert f(ws=ctypes.c_void_p(4096 + 8)) == -4              # 16-byte alignment
     assert f(n=2048 * 128) == -2                               # R beyond the selection limit
 
 
@@ -156,7 +158,8 @@ def test_similarity_argument_errors(lib):
     assert f(g=ctypes.byref(cbs.Grid(2, 20, 25, 21))) == -1         # anchors > rows
     assert f(g=ctypes.byref(cbs.Grid(2, 20, 25, 19))) == -2         # anchors = rows - 1
     assert f(prof=None) == -1
-    assert f(wsb=ws - 1) == -4
+    # a workspace for one head is enough (heads then go in chunks); less is not
+    assert f(wsb=cbs.calibatt_block_energy_workspace(1, 1000) - 1) == -4
     assert f(ws=None) == -4
     assert lib.calibatt_spatial_similarity(None, 0, 0, N, None, None, None, None) == 0
 

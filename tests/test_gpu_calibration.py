@@ -69,6 +69,38 @@ def test_energy_calibration_size_sampled(gpu, part):
         assert_energy_close(f64(e[h])[rows], want, f"energy head {h}")
 
 
+@pytest.mark.parametrize("name,heads_per_chunk", [("calibration_480p", 7), ("wan21_720p_layer", 3)])
+def test_energy_chunked_by_heads_is_bit_identical(gpu, name, heads_per_chunk):
+    """A workspace holding only a few heads makes calibatt_block_energy run
+    the heads in chunks; the energies equal those of one call over all heads
+    bit for bit (480p calibration shape, and the 720p layer shape whose full
+    workspace is 14.3 GB)."""
+    from synth import ATTN_WORKLOADS, qkv
+    if name in CALIB_WORKLOADS:
+        w = CALIB_WORKLOADS[name]
+        q, k = calib_draw(w, 1, calib_basis(w, DEV), DEV)
+        scale = w.scale
+    else:
+        w = ATTN_WORKLOADS[name]
+        q, k, _ = qkv(w, device=DEV)
+        scale = w.scale
+    H, N = q.shape[0], q.shape[1]
+    R = n_blocks(N)
+    say(f"case energy chunked {name} H={H} N={N}, {heads_per_chunk} heads per chunk")
+    full = torch.empty(H, R, R, dtype=torch.float32, device=DEV)
+    ws = torch.empty(gpu.calibatt_block_energy_workspace(H, N), dtype=torch.uint8, device=DEV)
+    gpu.calibatt_block_energy(q, k, full, scale, ws)
+    torch.cuda.synchronize()
+    del ws
+    part = torch.empty_like(full)
+    ws = torch.empty(gpu.calibatt_block_energy_workspace(heads_per_chunk, N) + 100,
+                     dtype=torch.uint8, device=DEV)
+    gpu.calibatt_block_energy(q, k, part, scale, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(full, part)
+    assert np.allclose(full.sum(dim=-1).cpu().numpy(), 1.0, atol=1e-5)
+
+
 def test_calibration_chain_on_gpu_energies_480p(gpu):
     """The calibration shape (40 heads, N = 32760, R = 256), four prompt
     draws: the library's own fp32 energies of all 40 heads go through
