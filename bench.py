@@ -227,10 +227,23 @@ def mfma_probe_case(cbs, iters: int = 20000, workgroups: int = 2048, reps: int =
     return flop / (ms * 1e-3) / 1e12, ms
 
 
+# VALU issue cost of one 128 x 128 energy tile (16384 scores, each an fma,
+# an exp2 and an add, 256 wave64 instructions of each): fma and add issue in
+# 4 cycles per wave64 instruction, v_exp_f32 in 8 (measured on the device).
+ENERGY_TILE_VALU_CYCLES = 256 * (4 + 8 + 4)
+SIMDS = 256 * 4
+NOMINAL_CLOCK_HZ = 2.4e9
+
+
 def calibration_case(cbs, draws: int):
-    """Calibration shape: energies of `draws` prompt draws, greedy selection
-    at eps(t) for the three steps, vote accumulation, then binarisation and
-    kept-list compilation. Returns per-stage times in ms."""
+    """The calibration pass as configured: 40 heads, N = 32760, `draws`
+    prompt draws; per draw the energy pass, the spatial-similarity score and
+    the greedy selection at eps(t) for t in {0, 25, 49} into votes; then for
+    each t binarisation at rho = 1/2 and kept-list compilation. Per-stage
+    device times from HIP events on the launch stream (the synthetic draws
+    are generated between the timed stages and not counted), the kept
+    fractions, and the keep-rate (vote fraction) histograms."""
+    from calibrated_block_sparse_amd.calibrate import vote_stats
     from synth import CALIB_WORKLOADS, calib_basis, calib_draw, n_blocks
     w = CALIB_WORKLOADS["calibration_480p"]
     R = n_blocks(w.n_tokens)
@@ -245,47 +258,105 @@ def calibration_case(cbs, draws: int):
     prof = torch.empty(w.heads, w.grid.frames * w.grid.rows, R, dtype=torch.float32, device="cuda")
     sim = torch.empty(w.heads, dtype=torch.float32, device="cuda")
     sim_sum = torch.zeros(w.heads, dtype=torch.float64, device="cuda")
-    t_energy = t_select = t_sim = 0.0
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(draws)]
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
     for p in range(draws):
         q, k = calib_draw(w, p, basis, "cuda")
-        torch.cuda.synchronize()
-        ev[0].record()
+        ev[p][0].record()
         cbs.calibatt_block_energy(q, k, energy, w.scale, ws)
-        ev[1].record()
+        ev[p][1].record()
         cbs.calibatt_spatial_similarity(ws, w.heads, w.n_tokens, grid, prof, sim)
-        ev[2].record()
+        ev[p][2].record()
         for t in w.steps:
             cbs.calibatt_build_mask(energy, efx[t], votes[t])
-        ev[3].record()
-        torch.cuda.synchronize()
+        ev[p][3].record()
         sim_sum += sim.double()
-        t_energy += ev[0].elapsed_time(ev[1])
-        t_sim += ev[1].elapsed_time(ev[2])
-        t_select += ev[2].elapsed_time(ev[3])
+    torch.cuda.synchronize()
+    t_energy = sum(e[0].elapsed_time(e[1]) for e in ev)
+    t_sim = sum(e[1].elapsed_time(e[2]) for e in ev)
+    t_select = sum(e[2].elapsed_time(e[3]) for e in ev)
     s_mean = (sim_sum / draws).cpu().numpy()
     mask = torch.empty(w.heads, R, R, dtype=torch.uint8, device="cuda")
     off = torch.empty(w.heads * R + 1, dtype=torch.int32, device="cuda")
     idx = torch.empty(w.heads * R * R, dtype=torch.int32, device="cuda")
-    t0 = time.perf_counter()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     kept = {}
+    t_fin = 0.0
     for t in w.steps:
+        e0.record()
         nnz = cbs.calibatt_finalize_mask(votes[t], draws, *w.rho, mask, off, idx)
+        e1.record()
+        torch.cuda.synchronize()
+        t_fin += e0.elapsed_time(e1)
         kept[t] = nnz / (w.heads * R * R)
-    t_fin = (time.perf_counter() - t0) * 1e3
-    flop_energy = 2.0 * w.heads * (R * 128) ** 2 * w.head_dim   # one Q K^T pass over every pair
+    t_wall = time.perf_counter() - t_wall
+    tiles = w.heads * R * R
+    flop_energy = 2.0 * tiles * 128 ** 3      # one Q K^T pass over every pair
+    e_ms = t_energy / draws
+    valu_bound_ms = tiles * ENERGY_TILE_VALU_CYCLES / (SIMDS * NOMINAL_CLOCK_HZ) * 1e3
     return {
         "workload": "calibration_480p", "heads": w.heads, "n_tokens": w.n_tokens, "draws": draws,
-        "energy_ms_per_draw": round(t_energy / draws, 3),
-        "energy_tflops": round(flop_energy / (t_energy / draws * 1e-3) / 1e12, 1),
+        "steps": list(w.steps), "rho": list(w.rho),
+        "device_ms_total": round(t_energy + t_sim + t_select + t_fin, 2),
+        "wall_s_incl_synthetic_draws": round(t_wall, 2),
+        "energy_ms_per_draw": round(e_ms, 3),
+        "energy_tflops": round(flop_energy / (e_ms * 1e-3) / 1e12, 1),
+        "energy_mfma_frac": round(flop_energy / (e_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "energy_valu_bound_ms": round(valu_bound_ms, 3),
+        "energy_valu_frac": round(valu_bound_ms / e_ms, 4),
         "select_votes_ms_per_draw_3eps": round(t_select / draws, 3),
         "similarity_ms_per_draw": round(t_sim / draws, 3),
+        "finalize_compile_ms_3steps": round(t_fin, 3),
         "similarity_mean_min_max": [round(float(s_mean.mean()), 4), round(float(s_mean.min()), 4),
                                     round(float(s_mean.max()), 4)],
         "repeat_heads_at_gamma_0_87": int((s_mean > 0.87).sum()),
-        "finalize_ms_3steps_incl_sync": round(t_fin, 3),
         "kept_fraction_by_step": {str(t): round(v, 4) for t, v in kept.items()},
+        "keep_rate_histogram_by_step": {str(t): vote_stats(votes[t], draws)["histogram"]
+                                        for t in w.steps},
+        "_energy_last_draw": energy,
     }
+
+
+def cpu_calibration_baseline(energy_gpu, seconds: float = 10.0):
+    """The fp64 oracle on one calibration draw: block energies of draw 0,
+    head 0, block-row by block-row for about `seconds`, extrapolated to all
+    heads and rows of the draw, plus the oracle's greedy selection at the
+    three eps(t) and binarisation over every head's rows (run in full, on the
+    library's energies of the last draw)."""
+    import oracle
+    from synth import CALIB_WORKLOADS, bf16_bits, calib_basis, calib_draw, n_blocks
+    w = CALIB_WORKLOADS["calibration_480p"]
+    R = n_blocks(w.n_tokens)
+    q, k = calib_draw(w, 0, calib_basis(w, "cpu"), "cpu", heads=1)
+    qb, kb = oracle.as_f64(bf16_bits(q[0])), oracle.as_f64(bf16_bits(k[0]))
+    t0 = time.perf_counter()
+    rows = 0
+    while time.perf_counter() - t0 < seconds and rows < R:
+        oracle.block_energy_row(qb, kb, w.scale, rows)
+        rows += 1
+    t_rows = time.perf_counter() - t0
+    E = energy_gpu.cpu().numpy().astype(np.float64)
+    t0 = time.perf_counter()
+    for t in w.steps:
+        eps = oracle.eps_fx(oracle.eps_schedule(t, w.total_steps, w.eps_floor, w.eps_start, w.eps_rate))
+        sel, _ = oracle.greedy_select(E, eps)
+        oracle.binarize(sel, 1, *w.rho)
+    t_sel = time.perf_counter() - t0
+    per_draw_s = t_rows / rows * R * w.heads + t_sel
+    return {"value": round(per_draw_s, 2), "unit": "s per calibration draw (40 heads, 3 eps)",
+            "cores": _blas_threads(), "kind": "oracle",
+            "sample": f"energy of head 0 block-rows 0..{rows - 1} of draw 0 ({t_rows:.1f} s, "
+                      f"extrapolated to {R} rows x {w.heads} heads); greedy selection at 3 eps and "
+                      f"binarisation of all 40 heads run in full ({t_sel:.1f} s)"}
+
+
+def _blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
+    except Exception:  # pragma: no cover
+        return int(os.cpu_count() or 1)
 
 
 def cpu_baseline(case, seconds: float = 15.0):
@@ -294,11 +365,7 @@ def cpu_baseline(case, seconds: float = 15.0):
     kept pairs it covered."""
     import oracle
     from synth import bf16_bits
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count()
+    cores = _blas_threads()
     w = case["workload"]
     mask = case["mask"]
     q, k, v = case["tensors"]
@@ -315,7 +382,8 @@ def cpu_baseline(case, seconds: float = 15.0):
         r += 1
     dt = time.perf_counter() - t0
     return {"value": round(pairs * PAIR_FLOP / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(cores),
-            "kind": "oracle",
+            "kind": "oracle", "host_cpu_count": os.cpu_count(),
+            "affinity": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None,
             "sample": f"{w.name} head 0, query blocks 0..{blocks - 1} ({pairs} kept pairs, fp64 numpy), {dt:.1f} s"}
 
 
@@ -339,7 +407,7 @@ def main():
     ap.add_argument("--workload", default="wan21_720p_layer")
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--calib-draws", type=int, default=4)
+    ap.add_argument("--calib-draws", type=int, default=64)
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-mask run")
     ap.add_argument("--no-sweep", action="store_true", help="skip the kept-fraction sweep")
     ap.add_argument("--copy-ref-mib", type=int, default=0,
@@ -445,11 +513,19 @@ def main():
         log("[bench] extra: mask bank")
         extras["mask_bank"] = bank_case(cbs, sp)
         log(f"[bench] extra: calibration, {args.calib_draws} draws")
-        extras["calibration"] = calibration_case(cbs, args.calib_draws)
+        cal = calibration_case(cbs, args.calib_draws)
+        e_last = cal.pop("_energy_last_draw")
+        extras["calibration"] = cal
         out["extras"] = extras
     if not args.no_cpu:
         log("[bench] cpu baseline (fp64 oracle)")
         out["cpu_baseline"] = cpu_baseline(sp)
+        if not args.no_extras:
+            log("[bench] cpu baseline of one calibration draw (fp64 oracle)")
+            cb = cpu_calibration_baseline(e_last)
+            cb["gpu_s_per_draw"] = round(out["extras"]["calibration"]["device_ms_total"]
+                                         / args.calib_draws / 1e3, 4)
+            out["extras"]["calibration"]["cpu_baseline"] = cb
     print(json.dumps(out), flush=True)
 
 
