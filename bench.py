@@ -305,6 +305,11 @@ def calibration_case(cbs, draws: int):
         "energy_mfma_frac": round(flop_energy / (e_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         "energy_valu_bound_ms": round(valu_bound_ms, 3),
         "energy_valu_frac": round(valu_bound_ms / e_ms, 4),
+        # a tile takes as many SIMD cycles of MFMA issue (2 * 128^3 FLOP at
+        # 1024 FLOP per cycle) as of VALU issue (4096): both bounds are equal,
+        # and their sum is the time with no overlap of the two
+        "energy_mfma_plus_valu_bound_ms": round(2 * valu_bound_ms, 3),
+        "energy_mfma_plus_valu_frac": round(2 * valu_bound_ms / e_ms, 4),
         "select_votes_ms_per_draw_3eps": round(t_select / draws, 3),
         "similarity_ms_per_draw": round(t_sim / draws, 3),
         "finalize_compile_ms_3steps": round(t_fin, 3),
