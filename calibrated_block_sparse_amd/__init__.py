@@ -101,11 +101,13 @@ _lib = None
 
 
 def load_library(path: Optional[str] = None):
-    """Loads libcalibatt.so once; raises if it is missing or lacks a symbol."""
+    """Loads libcalibatt.so once; raises if it is missing or lacks a symbol.
+    The environment variable CALIBATT_LIB names another build of the library
+    to load instead (for example the host-sanitized libcalibatt_asan.so)."""
     global _lib
     if _lib is not None and path is None:
         return _lib
-    p = path or LIB_PATH
+    p = path or os.environ.get("CALIBATT_LIB") or LIB_PATH
     if not os.path.exists(p):
         raise RuntimeError(f"{p} not found: build it with `python -m calibrated_block_sparse_amd.build`")
     lib = ctypes.CDLL(p)

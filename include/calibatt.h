@@ -414,8 +414,13 @@ int calibatt_bank_upload(calibatt_bank* bank, void* device, size_t bytes, void* 
 int calibatt_bank_lookup(const calibatt_bank* bank, int32_t t, int32_t l, int32_t on_device,
                          calibatt_bank_entry* out);
 
+/* ===========================================================================
+ * Diagnostics (not part of the method; no page defines them)
+ * ===========================================================================
+ */
+
 /*
- * Diagnostic, not part of the method: runs `workgroups` workgroups of four
+ * Matrix-core rate probe: runs `workgroups` workgroups of four
  * waves, each wave issuing iters x 8 independent bf16 32x32x16 MFMAs with
  * register operands (32768 FLOP each), i.e.
  *   workgroups * 4 * iters * 8 * 32768 FLOP,
