@@ -176,6 +176,37 @@ def bank_case(cbs, case, steps: int = 50, layers: int = 40, reps: int = 20):
             "bitwise_equal": bool(torch.equal(out_bank, o))}
 
 
+def noalloc_case(cbs, case, reps: int = 10):
+    """calibatt_sparse_attn_fwd_noalloc on the same layer and lists: its V^T
+    tiles go to the library's 256 MiB scratch, heads in chunks that fit
+    (pre-pass and attention per chunk); per-call time against the
+    workspace call (both including the V^T pre-pass), outputs compared."""
+    w = case["workload"]
+    q, k, v = case["tensors"]
+    off, idx = cbs.compile_skiplist(torch.from_numpy(case["mask"]).cuda())
+    o1, o2 = torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty(cbs.calibatt_sparse_attn_fwd_workspace(w.heads, w.n_tokens), dtype=torch.uint8,
+                     device="cuda")
+    fns = {"workspace": lambda: cbs.calibatt_sparse_attn_fwd(q, k, v, o1, off, idx, w.scale, workspace=ws),
+           "noalloc": lambda: cbs.calibatt_sparse_attn_fwd_noalloc(q, k, v, o2, off, idx, w.scale)}
+    ms = {}
+    for name, fn in fns.items():
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms[name] = e0.elapsed_time(e1) / reps
+    R = w.n_blocks
+    per = -(-w.heads // -(-w.heads // (8192 // R)))
+    return {"workload": w.name, "head_chunks": -(-w.heads // per), "heads_per_chunk": per,
+            "ms": round(ms["noalloc"], 3), "workspace_call_ms": round(ms["workspace"], 3),
+            "bitwise_equal": bool(torch.equal(o1, o2))}
+
+
 SWEEP_FRACTIONS = (1.0, 0.75, 0.5, 0.375, 0.25, 0.125)
 
 
@@ -517,6 +548,8 @@ def main():
         del c
         log("[bench] extra: mask bank")
         extras["mask_bank"] = bank_case(cbs, sp)
+        log("[bench] extra: attention without workspace (calibatt_sparse_attn_fwd_noalloc)")
+        extras["noalloc"] = noalloc_case(cbs, sp)
         log(f"[bench] extra: calibration, {args.calib_draws} draws")
         cal = calibration_case(cbs, args.calib_draws)
         e_last = cal.pop("_energy_last_draw")
