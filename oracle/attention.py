@@ -21,13 +21,15 @@ BLOCK = 128
 
 
 def as_f64(x) -> np.ndarray:
-    """fp64 copy of an input. uint16 / int16 arrays are raw bf16 bit
-    patterns and are decoded exactly (bf16 is the top half of an fp32)."""
+    """fp64 view of an input (the array itself when it is already fp64,
+    else a converted copy). uint16 / int16 arrays are raw bf16 bit patterns
+    and are decoded exactly (bf16 is the top half of an fp32). Callers never
+    write to the result."""
     a = np.asarray(x)
     if a.dtype in (np.uint16, np.int16):
         u32 = a.view(np.uint16).astype(np.uint32) << 16
         return u32.view(np.float32).astype(np.float64)
-    return a.astype(np.float64)
+    return np.asarray(a, dtype=np.float64)
 
 
 def _attend(qr: np.ndarray, kk: np.ndarray, vv: np.ndarray, scale: float) -> np.ndarray:
