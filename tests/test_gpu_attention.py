@@ -230,6 +230,25 @@ def test_full_size_layer_sampled(gpu, name, part, parts):
             say(f"  {name} head {h}: max-abs {e[0]:.2e} rel-fro {e[1]:.2e}")
 
 
+@pytest.mark.parametrize("name,head", [("wan21_720p_layer", 0), ("wan21_720p_layer", 39),
+                                       ("wan21_480p_layer", 7), ("wan21_480p_layer", 33)])
+def test_full_size_head_full_output(gpu, name, head):
+    """Every output token of one head of the full layer (all query blocks,
+    the launch covering all 40 heads as the bench times it) against the
+    oracle, block by block."""
+    w = ATTN_WORKLOADS[name]
+    say(f"case full output {name} head {head}")
+    q, k, v = qkv(w, device=DEV)
+    mask = block_mask(w)
+    o, _, _ = run(gpu, q, k, v, mask, w.scale)
+    qb, kb, vb = (oracle.as_f64(bf16_bits(t[head])) for t in (q, k, v))
+    want = np.concatenate([oracle.block_sparse_attention_block(qb, kb, vb, w.scale,
+                                                               np.flatnonzero(mask[head, r]), r)
+                           for r in range(w.n_blocks)])
+    e = assert_attn_close(f64(o[head]), want, f"{name} head {head}")
+    say(f"  max-abs {e[0]:.2e} rel-fro {e[1]:.2e} over {w.n_tokens} tokens")
+
+
 MOCHI_REPEAT_CASES = [(flag, part) for flag in (1, 2) for part in range(2)]
 
 
