@@ -258,10 +258,15 @@ def mfma_probe_case(cbs, iters: int = 20000, workgroups: int = 2048, reps: int =
     return flop / (ms * 1e-3) / 1e12, ms
 
 
-# VALU issue cost of one 128 x 128 energy tile (16384 scores, each an fma,
-# an exp2 and an add, 256 wave64 instructions of each): fma and add issue in
-# 4 cycles per wave64 instruction, v_exp_f32 in 8 (measured on the device).
-ENERGY_TILE_VALU_CYCLES = 256 * (4 + 8 + 4)
+# Issue cost of one 128 x 128 energy tile in SIMD cycles. VALU: 16384
+# scores, each an fma, an exp2 and an add (256 wave64 instructions of each);
+# fma and add at the published fp32 vector rate (157.3 TFLOP/s = 1024 SIMDs
+# x 2.4 GHz x 32 lanes x 2 FLOP: a wave64 instruction every 2 cycles),
+# v_exp_f32 at a quarter of it (8 cycles; a register-only probe with two
+# waves per SIMD measures 8.2 for v_exp_f32 and 2.7 for v_fma_f32). MFMA:
+# 2 * 128^3 FLOP at 1024 FLOP per cycle.
+ENERGY_TILE_VALU_CYCLES = 256 * (2 + 8 + 2)
+ENERGY_TILE_MFMA_CYCLES = 2 * 128 ** 3 // 1024
 SIMDS = 256 * 4
 NOMINAL_CLOCK_HZ = 2.4e9
 
@@ -326,6 +331,7 @@ def calibration_case(cbs, draws: int):
     flop_energy = 2.0 * tiles * 128 ** 3      # one Q K^T pass over every pair
     e_ms = t_energy / draws
     valu_bound_ms = tiles * ENERGY_TILE_VALU_CYCLES / (SIMDS * NOMINAL_CLOCK_HZ) * 1e3
+    mfma_bound_ms = tiles * ENERGY_TILE_MFMA_CYCLES / (SIMDS * NOMINAL_CLOCK_HZ) * 1e3
     return {
         "workload": "calibration_480p", "heads": w.heads, "n_tokens": w.n_tokens, "draws": draws,
         "steps": list(w.steps), "rho": list(w.rho),
@@ -334,13 +340,12 @@ def calibration_case(cbs, draws: int):
         "energy_ms_per_draw": round(e_ms, 3),
         "energy_tflops": round(flop_energy / (e_ms * 1e-3) / 1e12, 1),
         "energy_mfma_frac": round(flop_energy / (e_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "energy_mfma_bound_ms": round(mfma_bound_ms, 3),
         "energy_valu_bound_ms": round(valu_bound_ms, 3),
         "energy_valu_frac": round(valu_bound_ms / e_ms, 4),
-        # a tile takes as many SIMD cycles of MFMA issue (2 * 128^3 FLOP at
-        # 1024 FLOP per cycle) as of VALU issue (4096): both bounds are equal,
-        # and their sum is the time with no overlap of the two
-        "energy_mfma_plus_valu_bound_ms": round(2 * valu_bound_ms, 3),
-        "energy_mfma_plus_valu_frac": round(2 * valu_bound_ms / e_ms, 4),
+        # the time with no overlap of matrix-core and vector issue
+        "energy_mfma_plus_valu_bound_ms": round(mfma_bound_ms + valu_bound_ms, 3),
+        "energy_mfma_plus_valu_frac": round((mfma_bound_ms + valu_bound_ms) / e_ms, 4),
         "select_votes_ms_per_draw_3eps": round(t_select / draws, 3),
         "similarity_ms_per_draw": round(t_sim / draws, 3),
         "finalize_compile_ms_3steps": round(t_fin, 3),
