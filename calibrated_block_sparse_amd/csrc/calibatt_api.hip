@@ -7,9 +7,7 @@
 #include <cstdio>
 #include <cstring>
 #include <mutex>
-#include <string>
 #include <unordered_map>
-#include <vector>
 
 #include "../../include/calibatt.h"
 #include "kernels.h"
@@ -18,20 +16,20 @@ using namespace calibatt;
 
 namespace calibatt {
 
-thread_local std::string g_last_error;
+// The calling thread's last error message, in a fixed buffer: recording
+// one never allocates.
+thread_local char g_last_error[512];
 
 int api_fail(int code, const char* fmt, ...) {
-  char buf[512];
   va_list ap;
   va_start(ap, fmt);
-  vsnprintf(buf, sizeof buf, fmt, ap);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
   va_end(ap);
-  g_last_error = buf;
   return code;
 }
 
 int api_ok() {
-  g_last_error.clear();
+  g_last_error[0] = '\0';
   return CALIBATT_OK;
 }
 
@@ -97,7 +95,7 @@ int check_tensor_layout(const char* fn, int32_t heads, int32_t n_tokens, int32_t
 
 extern "C" {
 
-const char* calibatt_last_error(void) { return calibatt::g_last_error.c_str(); }
+const char* calibatt_last_error(void) { return calibatt::g_last_error; }
 
 int32_t calibatt_abi_version(void) { return 8; }
 
@@ -123,20 +121,20 @@ static int attn_core(const char* fn, const void* q, const void* k, const void* v
 
   const int32_t R = (int32_t)ceil_div(n_tokens, CALIBATT_BLOCK);
   if ((int64_t)heads * R > 0x7fffffff) return api_fail(CALIBATT_ERR_UNSUPPORTED, "%s: too many tiles", fn);
-  std::vector<int32_t> rep_heads, sparse_heads, masked_heads;
+  int32_t count[3] = {0, 0, 0};  // heads with flag 0 (block-sparse), 1 (repeat), 2 (masked repeat)
   for (int32_t h = 0; h < heads; ++h) {
     const int f = repeat_flags ? repeat_flags[h] : 0;
     if (f > 2)
       return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: repeat flag %d of head %d is not 0, 1 or 2", fn, f, h);
-    (f == 0 ? sparse_heads : f == 1 ? rep_heads : masked_heads).push_back(h);
+    ++count[f];
   }
-  if (!masked_heads.empty() && R > kMaxMaskedRepeatBlocks)
+  if (count[2] > 0 && R > kMaxMaskedRepeatBlocks)
     return api_fail(CALIBATT_ERR_UNSUPPORTED, "%s: masked repeat heads need R <= %d (R = %d)", fn,
                     kMaxMaskedRepeatBlocks, R);
 
   AttnArgs a;
   std::memset(&a, 0, sizeof a);
-  if (!rep_heads.empty() || !masked_heads.empty()) {
+  if (count[1] > 0 || count[2] > 0) {
     if (!grid) return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: repeat heads need a grid", fn);
     const int grc = check_grid(fn, *grid, n_tokens);
     if (grc) return grc;
@@ -146,7 +144,7 @@ static int attn_core(const char* fn, const void* q, const void* k, const void* v
     a.anchors = grid->anchors;
     a.anchor_queries = grid->frames * grid->anchors * grid->cols;
   }
-  if ((!sparse_heads.empty() || !masked_heads.empty()) && (!kv_offsets || (!kv_indices && nnz > 0)))
+  if ((count[0] > 0 || count[2] > 0) && (!kv_offsets || (!kv_indices && nnz > 0)))
     return api_fail(CALIBATT_ERR_INVALID_ARG, "%s: null kept-block list", fn);
 
   a.q = static_cast<const uint16_t*>(q);
@@ -164,16 +162,23 @@ static int attn_core(const char* fn, const void* q, const void* k, const void* v
   a.rep_tiles = (int32_t)ceil_div(a.anchor_queries, CALIBATT_BLOCK);
 
   // Launch in chunks of at most kMaxHeadsPerLaunch heads: masked repeat
-  // heads, plain repeat heads (the longest tiles first), then block-sparse.
+  // heads, plain repeat heads (the longest tiles first), then block-sparse,
+  // each kind in ascending head order. The heads of a kind are found by a
+  // cursor over the flags, so the call allocates nothing on the host either.
   a.mask_words = (int32_t)ceil_div(R, 32);
-  size_t mi = 0, ri = 0, si = 0;
-  while (mi < masked_heads.size() || ri < rep_heads.size() || si < sparse_heads.size()) {
+  auto next_of = [&](int kind, int32_t from) {
+    int32_t h = from;
+    while (h < heads && (repeat_flags ? repeat_flags[h] : 0) != kind) ++h;
+    return h;
+  };
+  int32_t hm = next_of(2, 0), hr = next_of(1, 0), hs = next_of(0, 0);
+  while (hm < heads || hr < heads || hs < heads) {
     int n = 0;
     a.n_mrep = a.n_rep = a.n_sparse = 0;
-    while (n < kMaxHeadsPerLaunch && mi < masked_heads.size()) { a.heads[n++] = masked_heads[mi++]; ++a.n_mrep; }
-    while (n < kMaxHeadsPerLaunch && ri < rep_heads.size()) { a.heads[n++] = rep_heads[ri++]; }
+    for (; n < kMaxHeadsPerLaunch && hm < heads; hm = next_of(2, hm + 1)) { a.heads[n++] = hm; ++a.n_mrep; }
+    for (; n < kMaxHeadsPerLaunch && hr < heads; hr = next_of(1, hr + 1)) a.heads[n++] = hr;
     a.n_rep = n;
-    while (n < kMaxHeadsPerLaunch && si < sparse_heads.size()) { a.heads[n++] = sparse_heads[si++]; ++a.n_sparse; }
+    for (; n < kMaxHeadsPerLaunch && hs < heads; hs = next_of(0, hs + 1)) { a.heads[n++] = hs; ++a.n_sparse; }
     const int64_t items = (int64_t)a.n_rep * a.rep_tiles + (int64_t)a.n_sparse * R;
     if (items > 0x7fffffff) return api_fail(CALIBATT_ERR_UNSUPPORTED, "%s: too many tiles", fn);
     a.n_items = (int32_t)items;
