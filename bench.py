@@ -38,7 +38,7 @@ PAIR_FLOP = 4.0 * 128 * 128 * 128  # QK^T and PV of one 128x128 block, D = 128
 METRIC = "effective TFLOP/s on kept blocks + speedup vs dense mask, Wan-720p shape, 1 GPU"
 KERNEL_SOURCES = ("calibrated_block_sparse_amd/csrc/attn_fwd.hip",
                   "calibrated_block_sparse_amd/csrc/device_common.h",
-                  "calibrated_block_sparse_amd/build.py")
+                  "calibrated_block_sparse_amd/csrc/kernels.h")
 
 
 def log(*a):
@@ -46,10 +46,15 @@ def log(*a):
 
 
 def kernel_hash() -> str:
+    """Hash of what the attention kernel's code is made from: its sources
+    and the compiler flags of the library build (paths left out, so that the
+    hash does not depend on where the tree sits)."""
+    from calibrated_block_sparse_amd.build import HIP_FLAGS
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
+    h.update(" ".join(f for f in HIP_FLAGS if not os.path.isabs(f)).encode())
     return h.hexdigest()[:16]
 
 
