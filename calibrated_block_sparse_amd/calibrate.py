@@ -87,15 +87,18 @@ def accumulate(draws: Iterable[Tuple[torch.Tensor, torch.Tensor]], scale: float,
                eps_fx: Dict[object, int], grid: Optional[Sequence[int]] = None) -> Calibration:
     """Run every draw (q, k: [H][N][128] bf16 CUDA) through the energy pass,
     the similarity score (when grid = (frames, rows, cols, anchors)) and the
-    greedy selection at each distinct eps. At most MAX_DRAWS draws (the
-    255th is the last one counted; a 256th raises ValueError before its
-    work is enqueued)."""
+    greedy selection at each distinct eps. Every draw has the first one's
+    shape and device. At most MAX_DRAWS draws (the 255th is the last one
+    counted; a 256th raises ValueError before its work is enqueued)."""
     by_eps = {}
     sim_sum = None
     n = 0
     for q, k in draws:
         if n == MAX_DRAWS:
             raise ValueError(f"more than {MAX_DRAWS} draws: votes are 8-bit counts")
+        if n > 0 and (tuple(q.shape[:2]) != (H, N) or q.device != energy.device):
+            raise ValueError(f"draw {n}: q is {tuple(q.shape)} on {q.device}, the first draw "
+                             f"was [{H}, {N}, 128] on {energy.device}")
         H, N, _ = q.shape
         R = n_blocks(N)
         if n == 0:

@@ -22,7 +22,6 @@ def test_more_than_255_draws_are_rejected():
         cal_mod.main(["--draws", "256"])
 
 
-
 def test_accumulate_stops_at_the_256th_draw(monkeypatch):
     """accumulate() counts draws and refuses the 256th before enqueueing its
     work (the library calls are replaced by counters here, so the test runs
@@ -40,6 +39,18 @@ def test_accumulate_stops_at_the_256th_draw(monkeypatch):
     with pytest.raises(ValueError, match="255"):
         cal_mod.accumulate(((q, q) for _ in range(256)), 0.1, {"a": 7})
     assert calls["energy"] == 255 + 255
+
+
+def test_accumulate_rejects_a_draw_of_another_shape(monkeypatch):
+    calls = []
+    monkeypatch.setattr(cal_mod, "calibatt_block_energy", lambda *a, **k: calls.append("e"))
+    monkeypatch.setattr(cal_mod, "calibatt_build_mask", lambda *a, **k: calls.append("s"))
+    monkeypatch.setattr(cal_mod, "calibatt_block_energy_workspace", lambda h, n: 8)
+    a = torch.zeros(2, 256, 128, dtype=torch.bfloat16)
+    b = torch.zeros(2, 384, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="draw 1"):
+        cal_mod.accumulate(iter([(a, a), (b, b)]), 0.1, {0: 7})
+    assert calls == ["e", "s"]   # nothing of the second draw was enqueued
 
 
 def test_schedule_variants_one_parameter_at_a_time():
