@@ -60,16 +60,17 @@ def test_noalloc_matches_workspace_call_on_shrinking_inputs(gpu):
 
 def test_noalloc_headline_layer(gpu):
     """Wan 720p layer (40 heads x 591 blocks: four chunks of 10 heads), then
-    the Mochi layer with repeat heads (one chunk): bit for bit against the
-    workspace call."""
-    for name in ("wan21_720p_layer", "mochi1_480p_layer"):
+    the Mochi layer (24 heads x 348 blocks: two chunks of 12, three repeat
+    heads in each) with its repeat heads plain (flag 1) and keeping their
+    block masks (flag 2): bit for bit against the workspace call."""
+    from synth import repeat_flags
+    for name, flag in (("wan21_720p_layer", 1), ("mochi1_480p_layer", 1), ("mochi1_480p_layer", 2)):
         w = ATTN_WORKLOADS[name]
-        say(f"case noalloc {name}")
+        say(f"case noalloc {name} repeat flag {flag}")
         q, k, v = qkv(w, device=DEV)
         off, idx = gpu.compile_skiplist(torch.from_numpy(block_mask(w)).to(DEV))
-        from synth import repeat_flags
-        fl = repeat_flags(w)
+        fl = repeat_flags(w) * np.uint8(flag)
         grid = (w.grid.frames, w.grid.rows, w.grid.cols, w.anchors) if fl.any() else None
         o_ws, o_na = both(gpu, q, k, v, off, idx, w.scale, fl if fl.any() else None, grid)
-        assert torch.equal(o_ws, o_na), name
+        assert torch.equal(o_ws, o_na), (name, flag)
         del q, k, v, o_ws, o_na
