@@ -66,10 +66,13 @@ typedef struct calibatt_grid {
   int32_t anchors;
 } calibatt_grid;
 
-/* Message of the last failed call on this thread ("" if none). */
+/* Message of this thread's last call that returned a status: its error, or
+ * "" when it succeeded. The buffer is per thread and stays valid until the
+ * thread's next such call. */
 const char* calibatt_last_error(void);
 
-/* Interface version (increments on any change of this header). Version 2
+/* Interface version (increments on any change of the declared interface:
+ * entry points, their arguments, structures, codes or contracts). Version 2
  * added the workspace of calibatt_sparse_attn_fwd, version 3 its two halves
  * calibatt_prepare_vt and calibatt_sparse_attn_fwd_vt, version 4 the
  * single-pass energy workspace and calibatt_mfma_rate_probe, version 5 the
