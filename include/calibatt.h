@@ -78,7 +78,8 @@ const char* calibatt_last_error(void);
  * single-pass energy workspace and calibatt_mfma_rate_probe, version 5 the
  * mask bank (calibatt_bank_*) and CALIBATT_ERR_IO, version 6
  * calibatt_spatial_similarity, version 7 masked repeat heads (flag 2),
- * version 8 calibatt_sparse_attn_fwd_noalloc. */
+ * version 8 calibatt_sparse_attn_fwd_noalloc, energy workspaces down to one
+ * head (heads then run in chunks) and the per-anchor grid rule. */
 int32_t calibatt_abi_version(void);
 
 /*
