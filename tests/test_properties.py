@@ -143,3 +143,69 @@ def test_validator_rejects_every_corruption(mask, data):
         assert e.code == -3
     else:
         raise AssertionError(f"corruption {kind} accepted")
+
+
+# ----------------------------------------------------------------------------
+# The oracle's attention and block energy on random small heads: properties
+# softmax attention has whatever the mask ([CalibAtt blog] §三 online
+# inference: a query block attends to the keys of its kept blocks only).
+
+ATT_SETTINGS = settings(max_examples=40, deadline=None,
+                        suppress_health_check=[HealthCheck.too_slow])
+heads = st.tuples(st.integers(min_value=1, max_value=400),      # N
+                  st.integers(min_value=0, max_value=2 ** 31),    # seed
+                  st.floats(min_value=0.0, max_value=1.0))        # keep probability
+
+
+def _head(N, seed, p, D=16):
+    rng = np.random.default_rng(seed)
+    q, k, v = (rng.standard_normal((N, D)) for _ in range(3))
+    R = (N + oracle.BLOCK - 1) // oracle.BLOCK
+    mask = (rng.random((R, R)) < p).astype(np.uint8)
+    return q, k, v, mask, 0.5 + rng.random()
+
+
+@ATT_SETTINGS
+@given(heads)
+def test_sparse_attention_rows_are_convex_combinations_of_kept_values(h):
+    """Every output row lies, coordinate by coordinate, between the least and
+    the greatest value of V over the keys of its block-row's kept blocks;
+    a block-row that keeps nothing is zero."""
+    q, k, v, mask, scale = _head(*h)
+    out = oracle.block_sparse_attention(q, k, v, scale, mask)
+    N = q.shape[0]
+    for r in range(mask.shape[0]):
+        rows = slice(r * oracle.BLOCK, min((r + 1) * oracle.BLOCK, N))
+        keys = oracle.kept_keys(np.flatnonzero(mask[r]), N)
+        if keys.size == 0:
+            assert not out[rows].any()
+            continue
+        lo, hi = v[keys].min(axis=0), v[keys].max(axis=0)
+        assert (out[rows] >= lo - 1e-12).all() and (out[rows] <= hi + 1e-12).all()
+
+
+@ATT_SETTINGS
+@given(heads, st.floats(min_value=-3, max_value=3), st.floats(min_value=-3, max_value=3))
+def test_sparse_attention_is_linear_in_the_values(h, a, b):
+    q, k, v, mask, scale = _head(*h)
+    v2 = np.random.default_rng(h[1] + 1).standard_normal(v.shape)
+    lhs = oracle.block_sparse_attention(q, k, a * v + b * v2, scale, mask)
+    rhs = a * oracle.block_sparse_attention(q, k, v, scale, mask) + \
+        b * oracle.block_sparse_attention(q, k, v2, scale, mask)
+    assert np.allclose(lhs, rhs, rtol=1e-10, atol=1e-10)
+
+
+@ATT_SETTINGS
+@given(heads)
+def test_attention_and_energy_ignore_a_common_key_shift(h):
+    """Adding one vector u to every key adds q_i.u to the whole score row i,
+    which the softmax over keys removes: the outputs and the block energies
+    are unchanged (a softmax taken over the wrong axis would not be)."""
+    q, k, v, mask, scale = _head(*h)
+    u = np.random.default_rng(h[1] + 2).standard_normal(k.shape[1])
+    ks = k + u[None, :]
+    assert np.allclose(oracle.block_sparse_attention(q, ks, v, scale, mask),
+                       oracle.block_sparse_attention(q, k, v, scale, mask), rtol=1e-9, atol=1e-11)
+    e0, e1 = oracle.block_energy(q, k, scale), oracle.block_energy(q, ks, scale)
+    assert np.allclose(e0, e1, rtol=1e-9, atol=1e-13)
+    assert np.allclose(e0.sum(axis=1), 1.0, atol=1e-12)
