@@ -253,15 +253,31 @@ __global__ void __launch_bounds__(kThreads) row_profile_kernel(const SimArgs a) 
   const float2* __restrict__ part = reinterpret_cast<const float2*>(a.partials) + (int64_t)head * R * np + i0;
   float* out = a.profiles + ((int64_t)head * FR + fy) * R;
   const float inv_w = 1.f / (float)W;
-  for (int c = wave; c < R; c += kThreads / 64) {
-    const float2* p = part + (int64_t)c * np;
-    float acc = 0.f;
+  // Each wave takes kProfileCols consecutive key blocks at a time and issues
+  // all their loads before any sum, so that many reads are in flight; the
+  // sum of each block is still lane x over x, x+64, ... then the butterfly.
+  constexpr int kProfileCols = 4;
+  for (int c0 = wave * kProfileCols; c0 < R; c0 += (kThreads / 64) * kProfileCols) {
+    float acc[kProfileCols];
+#pragma unroll
+    for (int u = 0; u < kProfileCols; ++u) acc[u] = 0.f;
     for (int x = lane; x < W; x += 64) {
-      const float2 v = p[x];
-      acc = __builtin_fmaf(v.x, __builtin_ldexpf(s_row[2 * x + 1], (int)(v.y - s_row[2 * x])), acc);
+      const float mi = s_row[2 * x], inv_l = s_row[2 * x + 1];
+      float2 v[kProfileCols];
+#pragma unroll
+      for (int u = 0; u < kProfileCols; ++u)
+        v[u] = c0 + u < R ? part[(int64_t)(c0 + u) * np + x] : float2{0.f, mi};
+#pragma unroll
+      for (int u = 0; u < kProfileCols; ++u)
+        acc[u] = __builtin_fmaf(v[u].x, __builtin_ldexpf(inv_l, (int)(v[u].y - mi)), acc[u]);
     }
-    acc = wave_sum(acc);
-    if (lane == 0) out[c] = acc * inv_w;
+#pragma unroll
+    for (int u = 0; u < kProfileCols; ++u) acc[u] = wave_sum(acc[u]);
+    if (lane == 0) {
+#pragma unroll
+      for (int u = 0; u < kProfileCols; ++u)
+        if (c0 + u < R) out[c0 + u] = acc[u] * inv_w;
+    }
   }
 }
 
