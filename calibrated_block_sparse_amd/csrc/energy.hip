@@ -168,11 +168,12 @@ __global__ void __launch_bounds__(kThreads, 2) energy_partials_kernel(const Ener
   if (g == 0 && qvalid) reinterpret_cast<float2*>(a.row_stats)[(int64_t)head * np + qi] = float2{m_run, ltot};
 }
 
-// One workgroup per (head, block-row r). Half-wave h of wave w takes key
-// blocks c = 2w + h, 2w + h + 8, ...; lane j of the half-wave reads the
-// partials of query rows 4j .. 4j+3 of block c (32 contiguous bytes, so a
-// half-wave reads block c's 128 partials as one 1 KiB run), sums its four
-// rows in order, and the 32 lanes combine by a fixed butterfly.
+// One workgroup per (head, block-row r). Wave w takes key blocks
+// 16w .. 16w+15, then 64 further on, ...; its half-wave h the blocks of
+// parity h among them. Lane j of the half-wave reads the partials of query
+// rows 4j .. 4j+3 of block c (32 contiguous bytes, so a half-wave reads
+// block c's 128 partials as one 1 KiB run), sums its four rows in order,
+// and the 32 lanes combine by a fixed butterfly.
 __global__ void __launch_bounds__(kThreads) energy_fixup_kernel(const EnergyArgs a) {
   __shared__ float s_m[kBlock], s_inv[kBlock];
   const int R = a.n_blocks, N = a.n_tokens;
@@ -201,21 +202,37 @@ __global__ void __launch_bounds__(kThreads) energy_fixup_kernel(const EnergyArgs
     f[k] = s_inv[i0 + k];
     m[k] = s_m[i0 + k];
   }
-  for (int c0 = 2 * wave; c0 < R; c0 += 2 * (kThreads / 64)) {
-    const int c = c0 + half;
-    float acc = 0.f;
-    if (c < R) {
-      const float4* p = reinterpret_cast<const float4*>(part + (int64_t)c * np);
-      const float4 v01 = p[0], v23 = p[1];
-      const float s[4] = {v01.x, v01.z, v23.x, v23.z};
-      const float e[4] = {v01.y, v01.w, v23.y, v23.w};
+  // Each half-wave takes kFixCols key blocks per pass and issues all their
+  // loads before summing, so several reads are in flight per wave.
+  constexpr int kFixCols = 8;
+  for (int c0 = 2 * kFixCols * wave; c0 < R; c0 += 2 * kFixCols * (kThreads / 64)) {
+    float4 v[kFixCols][2];
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-        if (i0 + k < rows) acc = __builtin_fmaf(s[k], __builtin_ldexpf(f[k], (int)(e[k] - m[k])), acc);
+    for (int u = 0; u < kFixCols; ++u) {
+      const int c = c0 + 2 * u + half;
+      if (c < R) {
+        const float4* p = reinterpret_cast<const float4*>(part + (int64_t)c * np);
+        v[u][0] = p[0];
+        v[u][1] = p[1];
+      } else {
+        v[u][0] = v[u][1] = float4{0.f, 0.f, 0.f, 0.f};
+      }
     }
 #pragma unroll
-    for (int o = 16; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 32);
-    if (j == 0 && c < R) out[c] = acc * inv_rows;
+    for (int u = 0; u < kFixCols; ++u) {
+      const int c = c0 + 2 * u + half;
+      float acc = 0.f;
+      if (c < R) {
+        const float s[4] = {v[u][0].x, v[u][0].z, v[u][1].x, v[u][1].z};
+        const float e[4] = {v[u][0].y, v[u][0].w, v[u][1].y, v[u][1].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (i0 + k < rows) acc = __builtin_fmaf(s[k], __builtin_ldexpf(f[k], (int)(e[k] - m[k])), acc);
+      }
+#pragma unroll
+      for (int o = 16; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 32);
+      if (j == 0 && c < R) out[c] = acc * inv_rows;
+    }
   }
 }
 
