@@ -90,12 +90,19 @@ __global__ void __launch_bounds__(kThreads, 2) energy_partials_kernel(const Ener
 
   copy_tile(lds0, kh, cp, 0, N, wave, lane);
 
+  // The record of block c is stored at the start of block c+1, after the
+  // wait: the wait (vmcnt counts stores too) then never waits for a store
+  // issued just before it.
+  float prev_row = 0.f, prev_ref = 0.f;
+  int prev_c = -1;
+
   // One block with its K tile in buffer kBuf.
   auto block = [&](auto kBufC, int c) {
     constexpr int kBuf = decltype(kBufC)::value;
     wait_vmem<0>();
     lds_barrier();  // K(c) landed; every wave is done with the other buffer
     if (c + 1 < R) copy_tile(lds0 + (1 - kBuf) * kTileBytes, kh, cp, (c + 1) * kBlock, N, wave, lane);
+    if (prev_c >= 0 && g == 0 && qvalid) part_out[(int64_t)prev_c * np] = float2{prev_row, prev_ref};
 
     f32x16 sacc[4];
 #pragma unroll
@@ -153,8 +160,9 @@ __global__ void __launch_bounds__(kThreads, 2) energy_partials_kernel(const Ener
       ps = partial(mref);
     }
     l_run += ps;
-    const float row = pair_sum_e(ps);
-    if (g == 0 && qvalid) part_out[(int64_t)c * np] = float2{row, mref};
+    prev_row = pair_sum_e(ps);
+    prev_ref = mref;
+    prev_c = c;
   };
 
   int c = 0;
@@ -164,6 +172,7 @@ __global__ void __launch_bounds__(kThreads, 2) energy_partials_kernel(const Ener
   }
   if (c < R) block(std::integral_constant<int, 0>{}, c);
 
+  if (prev_c >= 0 && g == 0 && qvalid) part_out[(int64_t)prev_c * np] = float2{prev_row, prev_ref};
   const float ltot = pair_sum_e(l_run);
   if (g == 0 && qvalid) reinterpret_cast<float2*>(a.row_stats)[(int64_t)head * np + qi] = float2{m_run, ltot};
 }
