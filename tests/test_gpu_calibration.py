@@ -281,7 +281,8 @@ def gpu_similarity(cbs, q, k, scale, grid):
 
 
 @pytest.mark.parametrize("F,Hs,W,kk,H,std", [(2, 20, 25, 5, 2, 1.5), (1, 8, 32, 2, 1, 1.0),
-                                             (3, 10, 13, 3, 2, 2.5), (2, 30, 7, 5, 1, 4.0)])
+                                             (3, 10, 13, 3, 2, 2.5), (2, 30, 7, 5, 1, 4.0),
+                                             (1, 4, 150, 2, 1, 1.5)])
 def test_similarity_matches_oracle(gpu, F, Hs, W, kk, H, std):
     N = F * Hs * W
     say(f"case similarity F={F} rows={Hs} cols={W} anchors={kk} H={H} std={std}")
