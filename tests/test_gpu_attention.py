@@ -522,6 +522,40 @@ def test_side_stream_scratch_is_not_reused_early(gpu):
         del junk, junk2
 
 
+def test_two_streams_in_flight_at_once(gpu):
+    """Independent calls on two streams with nothing ordering them (their own
+    workspaces and outputs; the library keeps no state between calls): the
+    results equal the same calls made one after the other."""
+    say("case two streams at once")
+    cases = []
+    for i, (H, N, p) in enumerate(((6, 12000, 0.5), (4, 9000, 0.3))):
+        q, k, v = (gaussian_bf16(560 + 10 * i + j, (H, N, 128)).to(DEV) for j in range(3))
+        mask = bernoulli_mask(565 + i, H, n_blocks(N), p, True)
+        off, idx = gpu.compile_skiplist(torch.from_numpy(mask).to(DEV))
+        ws = torch.empty(gpu.calibatt_sparse_attn_fwd_workspace(H, N), dtype=torch.uint8, device=DEV)
+        cases.append((q, k, v, off, idx, ws))
+    want = [gpu.sparse_attention(q, k, v, off, idx, 0.1) for q, k, v, off, idx, _ in cases]
+    want_e = gpu.block_energy(cases[1][0][:2], cases[1][1][:2], 0.1)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [torch.full_like(w, 3.0) for w in want]
+    e = torch.full_like(want_e, -1.0)
+    ews = torch.empty(gpu.calibatt_block_energy_workspace(2, cases[1][0].shape[1]), dtype=torch.uint8,
+                      device=DEV)
+    for st in streams:
+        st.wait_stream(torch.cuda.current_stream())
+    for rep in range(2):
+        for i, (q, k, v, off, idx, ws) in enumerate(cases):
+            gpu.calibatt_sparse_attn_fwd(q, k, v, outs[i], off, idx, 0.1, workspace=ws,
+                                         stream=streams[i])
+        gpu.calibatt_block_energy(cases[1][0][:2], cases[1][1][:2], e, 0.1, ews, stream=streams[1])
+        for st in streams:
+            st.synchronize()
+        for i in range(2):
+            assert torch.equal(outs[i], want[i]), (rep, i)
+        assert torch.equal(e, want_e), rep
+
+
 @pytest.mark.parametrize("N,H", [(1000, 2), (75600, 1)])
 def test_mask_that_keeps_nothing(gpu, N, H):
     """Every list empty (nnz = 0, an empty index tensor): the call succeeds
