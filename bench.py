@@ -461,7 +461,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
-              "(heads shard across GPUs without communication; see DESIGN.md)", file=sys.stderr)
+              "(heads would shard across GPUs without communication)", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
