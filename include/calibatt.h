@@ -22,8 +22,12 @@
  *   into heads.
  * - Every pointer named "device" is device memory owned by the caller. The
  *   library allocates no device memory and keeps no state between calls
- *   except the thread-local error string and the host memory of a mask bank
- *   handle (calibatt_bank_open .. calibatt_bank_close).
+ *   except the thread-local error string, the host memory of a mask bank
+ *   handle (calibatt_bank_open .. calibatt_bank_close) and the scratch of
+ *   calibatt_sparse_attn_fwd_noalloc: a static device array of
+ *   CALIBATT_NOALLOC_SCRATCH_BYTES that each device holds from the
+ *   library's load to the end of the process, and its device address,
+ *   looked up once per device.
  * - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
  *   and is asynchronous unless an entry point says otherwise. Argument
  *   errors are reported before anything is enqueued; launch failures return

@@ -74,3 +74,34 @@ def test_noalloc_headline_layer(gpu):
         o_ws, o_na = both(gpu, q, k, v, off, idx, w.scale, fl if fl.any() else None, grid)
         assert torch.equal(o_ws, o_na), (name, flag)
         del q, k, v, o_ws, o_na
+
+
+def test_noalloc_captured_in_a_graph(gpu):
+    """After a first eager call on the device, the no-alloc call captured in
+    a HIP graph (two head chunks: 40 heads x 256 blocks > 8192 tiles)
+    replays bit-identical to the workspace call on fresh inputs, with eager
+    work and synchronisation between the replays."""
+    H, N = 40, 32760
+    say("case noalloc graph capture")
+    q, k, v = (gaussian_bf16(600 + i, (H, N, 128)).to(DEV) for i in range(3))
+    mask = bernoulli_mask(603, H, n_blocks(N), 0.3, True)
+    off, idx = gpu.compile_skiplist(torch.from_numpy(mask).to(DEV))
+    o = torch.empty_like(q)
+    gpu.calibatt_sparse_attn_fwd_noalloc(q, k, v, o, off, idx, 0.1)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        gpu.calibatt_sparse_attn_fwd_noalloc(q, k, v, o, off, idx, 0.1, stream=side)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for i, t in enumerate((q, k, v)):
+            t.copy_(gaussian_bf16(610 + 10 * rep + i, (H, N, 128)).to(DEV))
+        want = torch.empty_like(q)
+        gpu.calibatt_sparse_attn_fwd(q, k, v, want, off, idx, 0.1)
+        torch.cuda.synchronize()
+        o.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, want), f"replay {rep}"
