@@ -8,11 +8,14 @@
  * (R = ceil(N / 128)). The program uploads them, compiles the mask into
  * kept-block lists on the device (calibatt_compile_skiplist), runs
  * calibatt_sparse_attn_fwd on the default stream and writes the bf16 bits
- * of o to OUT. Exit status 0 on success. */
+ * of o to OUT; it also runs calibatt_sparse_attn_fwd_noalloc (no workspace)
+ * and reports whether its output is byte-identical. Exit status 0 on
+ * success. */
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
+#include <string.h>
 
 #include "calibatt.h"
 
@@ -47,7 +50,7 @@ int main(int argc, char** argv) {
   if (!host || !mask || read_all(in, host, 3 * tbytes) || read_all(in, mask, mbytes)) return 1;
   fclose(in);
 
-  void *q, *k, *v, *o, *ws;
+  void *q, *k, *v, *o, *o2, *ws;
   uint8_t* d_mask;
   int32_t *off, *idx;
   const size_t ws_bytes = calibatt_sparse_attn_fwd_workspace(H, N);
@@ -55,6 +58,7 @@ int main(int argc, char** argv) {
   HIP_OK(hipMalloc(&k, tbytes));
   HIP_OK(hipMalloc(&v, tbytes));
   HIP_OK(hipMalloc(&o, tbytes));
+  HIP_OK(hipMalloc(&o2, tbytes));
   HIP_OK(hipMalloc(&ws, ws_bytes));
   HIP_OK(hipMalloc((void**)&d_mask, mbytes));
   HIP_OK(hipMalloc((void**)&off, ((size_t)H * R + 1) * 4));
@@ -76,8 +80,16 @@ int main(int argc, char** argv) {
     fprintf(stderr, "calibatt_sparse_attn_fwd: %d %s\n", rc, calibatt_last_error());
     return 3;
   }
+  rc = calibatt_sparse_attn_fwd_noalloc(q, k, v, o2, H, N, 128, (int64_t)N * 128, 128, scale, off, idx,
+                                        nnz, NULL, NULL, NULL);
+  if (rc != CALIBATT_OK) {
+    fprintf(stderr, "calibatt_sparse_attn_fwd_noalloc: %d %s\n", rc, calibatt_last_error());
+    return 3;
+  }
   HIP_OK(hipDeviceSynchronize());
   HIP_OK(hipMemcpy(host, o, tbytes, hipMemcpyDeviceToHost));
+  HIP_OK(hipMemcpy((char*)host + tbytes, o2, tbytes, hipMemcpyDeviceToHost));
+  const int same = memcmp(host, (const char*)host + tbytes, tbytes) == 0;
   FILE* out = fopen(argv[2], "wb");
   if (!out || fwrite(host, 1, tbytes, out) != tbytes) return 1;
   fclose(out);
@@ -85,12 +97,13 @@ int main(int argc, char** argv) {
   hipFree(k);
   hipFree(v);
   hipFree(o);
+  hipFree(o2);
   hipFree(ws);
   hipFree(d_mask);
   hipFree(off);
   hipFree(idx);
   free(host);
   free(mask);
-  printf("ok nnz=%lld\n", (long long)nnz);
+  printf("ok nnz=%lld noalloc=%s\n", (long long)nnz, same ? "equal" : "different");
   return 0;
 }

@@ -2,7 +2,8 @@
 (tests/c_consumer/attn_gpu.c: HIP runtime API and include/calibatt.h only,
 no torch in its process). It compiles the mask into kept lists on the
 device and runs calibatt_sparse_attn_fwd; its output matches the oracle
-(max-abs <= 2e-2, rel-Frobenius <= 1e-2)."""
+(max-abs <= 2e-2, rel-Frobenius <= 1e-2), and calibatt_sparse_attn_fwd_noalloc
+called from the same program gives the same bytes."""
 
 import os
 import shutil
@@ -47,7 +48,7 @@ def test_attention_from_plain_c(tmp_path):
     r = subprocess.run([exe, str(src), str(dst)], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stderr
     say(f"  {r.stdout.strip()}")
-    assert r.stdout.strip() == f"ok nnz={int(mask.sum())}"
+    assert r.stdout.strip() == f"ok nnz={int(mask.sum())} noalloc=equal"
     out = np.fromfile(dst, dtype=np.uint16).reshape(H, N, 128)
     got = (out.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     for h in range(H):
